@@ -1,0 +1,35 @@
+"""CPU oracle for the fused weight-gradient GEMM + optimizer step.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this package: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP library.
+
+What it computes is the plain, unfused definition of the method described on
+the page "docs(audit): FORGE assessment + residency-aware epilogue-fusion
+track" (Tessera PR 565): the weight gradient dW = X^T dY reduced over all
+tokens (section "What's already in tree and easy to miss", the transposed-lhs
+matmul), rounded once to float32, then an ordinary float32 AdamW or
+SGD-momentum step (section "Claim hygiene on the source": the public release
+ships AdamW and SGD only). Fusion changes where the gradient lives, not its
+value (section "Math verified, not asserted", P1), so the unfused definition
+is the reference for the fused kernels.
+
+Parity pins (tests that check this package against closed forms, exact
+rational arithmetic and invariants) live in tests/test_oracle_pins.py.
+Parity unpinned: the exact summation order inside the GPU contraction (only
+the accumulation floor in ``floor.py`` bounds it), and the magnitudes the page
+quotes without their setups (2.24x at 50% routing, ~900x / ~1x).
+"""
+from .ref import (  # noqa: F401
+    ClipNotFusable,
+    adamw_moments,
+    adamw_param,
+    adamw_step,
+    bf16_bits_to_f64,
+    grouped_adamw_step,
+    grouped_wgrad,
+    sgdm_step,
+    wgrad,
+    wgrad_rows,
+)
+from .floor import StateFloor, acc_floor, acc_floor_rows  # noqa: F401

@@ -1,0 +1,59 @@
+"""Accumulation floor: how far a correct float32-accumulated gradient may sit
+from the oracle's correctly rounded one, and how that gap carries into the
+optimizer state.
+
+TEST INFRASTRUCTURE ONLY. Any summation order of T float32 additions is a
+correct weight gradient; the page fixes none. With unit roundoff u = 2^-24 and
+s[o, i] = sqrt(sum_t (dY[t, o] X[t, i])^2), a random-walk estimate of the
+error of a float32 running sum is u sqrt(T) s; the floor takes four times it:
+
+    tau[o, i] = 4 * 2^-24 * sqrt(T) * s[o, i]
+
+and carries it through the moment recurrences
+    m_err_t = beta1 m_err_{t-1} + (1 - beta1) tau_t
+    v_err_t = beta2 v_err_{t-1} + (1 - beta2) (2 |g_t| tau_t + tau_t^2)
+(SGD-momentum: b_err_t = momentum b_err_{t-1} + tau_t).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .ref import bf16_bits_to_f64
+
+U32 = 2.0 ** -24
+
+
+def acc_floor(X_bits: np.ndarray, dY_bits: np.ndarray) -> np.ndarray:
+    """tau in the weight's [d_out, d_in] layout (float64)."""
+    X = bf16_bits_to_f64(X_bits)
+    dY = bf16_bits_to_f64(dY_bits)
+    T = X.shape[0]
+    s2 = (dY * dY).T @ (X * X)
+    return 4.0 * U32 * np.sqrt(max(T, 1)) * np.sqrt(s2)
+
+
+def acc_floor_rows(X_bits: np.ndarray, dY_bits: np.ndarray, rows) -> np.ndarray:
+    rows = np.asarray(rows, dtype=np.int64)
+    return acc_floor(X_bits, np.ascontiguousarray(dY_bits[:, rows]))
+
+
+class StateFloor:
+    """Propagated floors for the optimizer state of one tensor (or a sample)."""
+
+    def __init__(self, shape, kind: str = "adamw", beta1: float = 0.9, beta2: float = 0.999,
+                 momentum: float = 0.9):
+        self.kind = kind
+        self.beta1, self.beta2, self.momentum = beta1, beta2, momentum
+        self.m_err = np.zeros(shape, dtype=np.float64)
+        self.v_err = np.zeros(shape, dtype=np.float64)
+
+    def update(self, tau: np.ndarray, g_ref: np.ndarray) -> None:
+        tau = np.asarray(tau, dtype=np.float64)
+        if self.kind == "adamw":
+            g = np.abs(np.asarray(g_ref, dtype=np.float64))
+            self.m_err = self.beta1 * self.m_err + (1.0 - self.beta1) * tau
+            self.v_err = self.beta2 * self.v_err + (1.0 - self.beta2) * (2.0 * g * tau + tau * tau)
+        elif self.kind == "sgdm":
+            self.m_err = self.momentum * self.m_err + tau
+        else:
+            raise ValueError(self.kind)
