@@ -1,0 +1,285 @@
+"""Benchmark of the fused weight-gradient GEMM + optimizer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mlp_down] [--no-cpu]
+
+One step = one fused call over one batch of seeded synthetic input already
+resident in HBM: dW = X^T dY (bf16 in, fp32 accumulate, all tokens) consumed by
+AdamW in the epilogue, W/m/v updated in place. The default workload is a
+Llama-3-8B MLP down projection (X [8192, 14336], dY [8192, 4096], fp32 W/m/v
+[4096, 14336]). The unfused pair (fp32 gradient stored, then elementwise AdamW)
+is timed beside it, and the CPU oracle on a bounded sample.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused dW-GEMM+AdamW TFLOP/s & ms/step, MFMA util %, HBM bytes vs unfused"
+
+WORKLOADS = {
+    # name: (config index, optimizer)
+    "tiny": (0, "adamw"),
+    "mlp_down": (1, "adamw"),
+    "qkv": (2, "adamw"),
+    "qkv_sgdm": (2, "sgdm"),
+    "lm_head": (3, "adamw"),
+    "moe": (4, "adamw"),
+}
+KERNEL_SOURCES = ("wgrad_kernels.hpp", "optim_math.hpp", "forge.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "weight_gradient_gemm_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    m_sha = re.search(r"^kernel_source_sha:\s*(\w+)", text, re.M)
+    m_b = re.search(r"^fused_hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not (m_sha and m_b) or m_sha.group(1) != sha:
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mlp_down", choices=sorted(WORKLOADS))
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--pool", type=int, default=2, help="distinct input batches cycled")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the fused kernel needs no collective, and "
+              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_gradient_gemm_amd as wg
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    k, opt = WORKLOADS[args.workload]
+    case = synth.CONFIGS[k]
+    grouped = isinstance(case, synth.GroupedCase)
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    log(f"[bench] workload {args.workload}: {case}")
+    t0 = time.perf_counter()
+    batches = []
+    for s in range(1, args.pool + 1):
+        if grouped:
+            Xp, Yp, offs = synth.grouped_inputs(case, s)
+            batches.append((up_bf16(Xp), up_bf16(Yp), [int(x) for x in offs], (Xp, Yp, offs)))
+        else:
+            Xb, Yb = synth.dense_inputs(case, s)
+            batches.append((up_bf16(Xb), up_bf16(Yb), None, (Xb, Yb, None)))
+        log(f"[bench] batch {s} ready ({time.perf_counter() - t0:.1f}s)")
+    W0, m0, v0 = synth.grouped_state(case) if grouped else synth.dense_state(case)
+    W = torch.from_numpy(W0).to(dev)
+    m = torch.from_numpy(m0).to(dev)
+    v = torch.from_numpy(v0).to(dev)
+    if grouped:
+        rows = int(batches[0][2][-1])
+        flops = 2 * rows * case.d_in * case.d_out
+        n_param = case.E * case.d_in * case.d_out
+        x_bytes = 2 * rows * (case.d_in + case.d_out)
+    else:
+        flops = 2 * case.T * case.d_in * case.d_out
+        n_param = case.d_in * case.d_out
+        x_bytes = 2 * case.T * (case.d_in + case.d_out)
+    state_bytes = (24 if opt == "adamw" else 16) * n_param
+    alg_bytes = x_bytes + state_bytes
+    hp = dict(lr=case.lr, weight_decay=case.weight_decay)
+    if opt == "adamw":
+        hp.update(beta1=case.beta1, beta2=case.beta2, eps=case.eps)
+    else:
+        hp.update(momentum=case.momentum)
+        hp["weight_decay"] = 0.0
+
+    def fused(step, batch):
+        X, dY, offs, _ = batch
+        if grouped:
+            wg.forge_grouped_wgrad_adamw(X, dY, offs, W, m, v, step=step, tile=args.tile, **hp)
+        elif opt == "adamw":
+            wg.forge_wgrad_adamw(X, dY, W, m, v, step=step, tile=args.tile, **hp)
+        else:
+            wg.forge_wgrad_sgdm(X, dY, W, m, tile=args.tile, **hp)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps, warmup, per_launch_events=True):
+        for s in range(warmup):
+            fn(s + 1, batches[s % len(batches)])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for s in range(steps):
+            ev[s][0].record(stream)
+            fn(warmup + s + 1, batches[(warmup + s) % len(batches)])
+            ev[s][1].record(stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total = t_start.elapsed_time(t_end)
+        per = [a.elapsed_time(b) for a, b in ev]
+        return total / steps, float(np.mean(per)), per
+
+    ms_step, ms_kernel, per = timed(fused, args.steps, args.warmup)
+    log(f"[bench] fused: {ms_step:.4f} ms/step, kernel avg {ms_kernel:.4f} ms "
+        f"(min {min(per):.4f} max {max(per):.4f})")
+
+    unfused = None
+    if not args.no_unfused and not grouped:
+        grad = torch.empty_like(W)
+
+        def unfused_step(step, batch):
+            X, dY, _, _ = batch
+            wg.forge_wgrad(X, dY, grad, tile=args.tile)
+            if opt == "adamw":
+                wg.forge_adamw(grad, W, m, v, step=step, **hp)
+            else:
+                wg.forge_sgdm(grad, W, m, **hp)
+
+        u_step, u_kernel, _ = timed(unfused_step, args.steps, args.warmup)
+        unfused = {"ms_per_step": round(u_step, 5), "tflops": round(flops / u_step / 1e9, 2),
+                   "alg_hbm_bytes": alg_bytes + 8 * n_param,
+                   "fused_speedup": round(u_step / ms_step, 4)}
+        log(f"[bench] unfused: {u_step:.4f} ms/step")
+        del grad
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {args.copy_calib_mib} MiB copied")
+
+    value = flops / ms_step / 1e9
+    achieved = flops / ms_kernel / 1e9
+    sha = kernel_source_sha()
+    traffic = read_traffic(args.workload, sha)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                           if p.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        Xb, Yb, offs = batches[0][3]
+        Wc, mc, vc = W0.copy(), m0.copy(), v0.copy()
+        ahp = dict(lr=case.lr, beta1=case.beta1, beta2=case.beta2, eps=case.eps,
+                   weight_decay=case.weight_decay)
+        log("[bench] CPU oracle leg ...")
+        c0 = time.perf_counter()
+        if grouped:
+            grads = oracle.grouped_wgrad(Xb, Yb, offs)
+            oracle.grouped_adamw_step(Wc, mc, vc, grads, 1, **ahp)
+            sample = f"one full oracle step of {args.workload} (grouped fp64 GEMMs + fp32 AdamW)"
+        else:
+            g = oracle.wgrad(Xb, Yb)
+            if opt == "adamw":
+                oracle.adamw_step(Wc, mc, vc, g, 1, **ahp)
+            else:
+                oracle.sgdm_step(Wc, mc, g, lr=case.lr, momentum=case.momentum)
+            sample = (f"one full oracle step of {args.workload} "
+                      f"(fp64 GEMM {case.T}x{case.d_in}x{case.d_out} + fp32 {opt})")
+        c_s = time.perf_counter() - c0
+        cpu = {"value": round(flops / c_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+               "kind": "oracle", "sample": sample, "seconds": round(c_s, 3),
+               "host_cpus": os.cpu_count()}
+        log(f"[bench] CPU oracle: {c_s:.2f} s")
+
+    if grouped:
+        wl = (f"{case.name}: {case.E} experts W[{case.d_out},{case.d_in}] fp32, "
+              f"{rows} routed rows, AdamW")
+        cfg = {"workload": wl, "experts": case.E, "routed_rows": rows, "d_in": case.d_in,
+               "d_out": case.d_out, "optimizer": opt, "tile": args.tile}
+    else:
+        wl = (f"{case.name}: X bf16[{case.T},{case.d_in}] dY bf16[{case.T},{case.d_out}] "
+              f"W/m/v fp32[{case.d_out},{case.d_in}], {opt}")
+        cfg = {"workload": wl, "T": case.T, "d_in": case.d_in, "d_out": case.d_out,
+               "optimizer": opt, "tile": args.tile}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": cfg,
+        "mfma_util_pct": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_ms": round(ms_kernel, 5),
+        "alg_hbm_bytes": alg_bytes,
+        "alg_hbm_gbs": round(alg_bytes / ms_kernel / 1e6, 1),
+        "hbm_frac_alg": round(alg_bytes / ms_kernel / 1e6 / PEAK_HBM_GBS, 4),
+        "unfused": unfused,
+        "kernel_source_sha": sha,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * forge.h - C ABI of the fused weight-gradient GEMM + optimizer library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation. For a linear layer with forward input X [T, d_in] and output
+ * gradient dY [T, d_out] (both bfloat16, row-major), the weight gradient is the
+ * contraction over all T tokens
+ *
+ *     g[o, i] = sum_t dY[t, o] * X[t, i]          (g has W's [d_out, d_in] layout)
+ *
+ * i.e. dW = X^T dY written in the weight's layout. The fused entry points feed
+ * each output tile's float32 accumulator straight into the optimizer step
+ * (AdamW or SGD-momentum) and update W and its state in place, so the
+ * gradient is never written to memory. Source: the page "docs(audit): FORGE
+ * assessment + residency-aware epilogue-fusion track" (Tessera PR 565),
+ * introduction (the optimizer step runs in the weight-gradient GEMM's
+ * epilogue, per tile, and the gradient never reaches HBM) and section
+ * "What's already in tree and easy to miss" (the weight gradient is the
+ * transposed-lhs matmul, with its reduction kept whole per output tile).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer named X, dY, W, m, v, mom, grad is a DEVICE pointer owned
+ *     by the caller; the library allocates nothing and keeps no state between
+ *     calls except a per-device architecture check. bfloat16 arrays are passed
+ *     as raw 16-bit storage. All arrays are dense row-major.
+ *   - W, m, v, mom are float32 and updated in place. X and dY are read only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous and stream-ordered; FORGE_OK means "validated and
+ *     launched". Results are ready once the stream reaches the call.
+ *   - Validation happens before anything is launched; on any error nothing is
+ *     launched and no buffer is read or written.
+ *   - Alignment: every device pointer 16-byte aligned, d_in % 8 == 0 and
+ *     d_out % 8 == 0 (FORGE_ERR_ALIGN otherwise; there is no scalar fallback).
+ *   - W, m, v (and mom) must not overlap each other, X or dY (FORGE_ERR_ALIAS).
+ *   - T == 0 is allowed: the gradient is exactly zero and the optimizer takes
+ *     a pure decay step. X and dY may then be NULL. d_in == 0 or d_out == 0 is
+ *     a no-op that returns FORGE_OK.
+ *   - Non-finite values are not checked; they propagate as in unfused code.
+ *   - The device must be gfx950; any other device returns FORGE_ERR_DEVICE
+ *     (there is no fallback path).
+ *
+ * Caller preconditions that the library cannot check:
+ *   - X^T dY of this call is the complete gradient of W for this step: the
+ *     weight is used once (no tied weights, no accumulation across calls).
+ *     FORGE assessment, "Math verified, not asserted", P1: a tied weight's
+ *     gradient is a sum of two products, so the fusion does not apply.
+ *   - Any computation that needs the pre-update W (e.g. dX = dY W) has been
+ *     issued on `stream` (or completed) before this call: the update is in
+ *     place. FORGE assessment, P1, the in-place dX-before-update hazard.
+ *   - No other stream reads or writes W, m, v while the call runs.
+ *
+ * Determinism: every output element accumulates its tokens in ascending
+ * order, 16 at a time, in one accumulator, with no split of the reduction
+ * and no atomics. The result is therefore bitwise identical for every tile
+ * choice, between fused and unfused paths, and from run to run (FORGE
+ * assessment, P1: per-tile exactness is bitwise and partition independent).
+ */
+#ifndef FORGE_H
+#define FORGE_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FORGE_API __attribute__((visibility("default")))
+#else
+#define FORGE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t forge_status;
+
+enum {
+  FORGE_OK = 0,
+  FORGE_ERR_NULL = 1,             /* a required pointer is NULL                          */
+  FORGE_ERR_SHAPE = 2,            /* negative size, or a size beyond the library's range */
+  FORGE_ERR_ALIGN = 3,            /* pointer not 16-byte aligned, or d_in/d_out % 8 != 0 */
+  FORGE_ERR_ALIAS = 4,            /* output buffers overlap each other or an input       */
+  FORGE_ERR_HPARAM = 5,           /* hyperparameter out of range (see the structs)       */
+  FORGE_ERR_CLIP_NOT_FUSABLE = 6, /* a global-norm clip was requested                    */
+  FORGE_ERR_TILE = 7,             /* unknown tile id                                     */
+  FORGE_ERR_DEVICE = 8,           /* current device is not gfx950, or no device          */
+  FORGE_ERR_LAUNCH = 9            /* the HIP runtime rejected the launch                 */
+};
+
+/*
+ * AdamW with decoupled weight decay, float32 state. For step t (1-based):
+ *   m_t = beta1 m_{t-1} + (1 - beta1) g
+ *   v_t = beta2 v_{t-1} + (1 - beta2) g^2
+ *   W_t = W_{t-1} (1 - lr wd) - lr / (1 - beta1^t) * m_t / (sqrt(v_t) / sqrt(1 - beta2^t) + eps)
+ * The scalars in the last line are formed on the host in double precision and
+ * rounded to float32; the per-element arithmetic is float32, IEEE-rounded.
+ * FORGE assessment, "Claim hygiene on the source": AdamW and SGD are the
+ * optimizers the method covers.
+ * Ranges: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0, weight_decay >= 0,
+ * all finite; step >= 1 (all experts of a grouped call share it).
+ * max_grad_norm must be 0. Any value > 0 (including +inf) returns
+ * FORGE_ERR_CLIP_NOT_FUSABLE: FORGE assessment, "Math verified, not asserted",
+ * P2 - exact global-norm clipping needs the norm of the whole gradient before
+ * any tile's moments are updated, so it cannot run in a per-tile epilogue and
+ * a request must fail closed. Negative or NaN: FORGE_ERR_HPARAM.
+ */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+  int64_t step;
+  double max_grad_norm;
+} forge_adamw_params;
+
+/*
+ * SGD with momentum (coupled weight decay, no dampening, no Nesterov):
+ *   b_t = momentum b_{t-1} + (g + wd W_{t-1});   W_t = W_{t-1} - lr b_t
+ * With a zero buffer, the first step gives b_1 = g + wd W_0.
+ * Ranges: lr >= 0, 0 <= momentum < 1, weight_decay >= 0, all finite;
+ * max_grad_norm as for AdamW.
+ */
+typedef struct {
+  double lr;
+  double momentum;
+  double weight_decay;
+  double max_grad_norm;
+} forge_sgdm_params;
+
+/*
+ * Output tile of one workgroup, named (d_in extent) x (d_out extent).
+ * Every tile gives bitwise-identical results; only speed differs.
+ */
+typedef int32_t forge_tile;
+enum {
+  FORGE_TILE_DEFAULT = 0,   /* library's choice for the shape                     */
+  FORGE_TILE_256x128 = 1,
+  FORGE_TILE_128x128 = 2,
+  FORGE_TILE_COUNT = 3
+};
+
+/* Maximum number of experts in one grouped call. */
+#define FORGE_MAX_EXPERTS 256
+
+/*
+ * Fused weight gradient + AdamW.
+ *   X  [T, d_in]  bf16     dY [T, d_out] bf16
+ *   W, m, v [d_out, d_in] float32, updated in place.
+ */
+FORGE_API forge_status forge_wgrad_adamw(const void* X, const void* dY, float* W, float* m, float* v,
+                               int64_t T, int64_t d_in, int64_t d_out,
+                               const forge_adamw_params* p, forge_tile tile, void* stream);
+
+/*
+ * Fused weight gradient + SGD-momentum.
+ *   W, mom [d_out, d_in] float32, updated in place.
+ */
+FORGE_API forge_status forge_wgrad_sgdm(const void* X, const void* dY, float* W, float* mom,
+                              int64_t T, int64_t d_in, int64_t d_out,
+                              const forge_sgdm_params* p, forge_tile tile, void* stream);
+
+/*
+ * Unfused comparison, first half: writes the float32 gradient grad [d_out, d_in]
+ * (overwritten, not accumulated). Same contraction, tile and order as the fused
+ * calls, so grad is bitwise the gradient the fused calls consume.
+ */
+FORGE_API forge_status forge_wgrad(const void* X, const void* dY, float* grad,
+                         int64_t T, int64_t d_in, int64_t d_out, forge_tile tile, void* stream);
+
+/*
+ * Unfused comparison, second half: elementwise AdamW on n float32 elements,
+ * reading grad and updating W, m, v in place. Same per-element arithmetic as
+ * the fused epilogue. n >= 0; pointers 16-byte aligned (any n).
+ */
+FORGE_API forge_status forge_adamw(const float* grad, float* W, float* m, float* v, int64_t n,
+                         const forge_adamw_params* p, void* stream);
+
+/* Unfused elementwise SGD-momentum on n elements (same contract as forge_adamw). */
+FORGE_API forge_status forge_sgdm(const float* grad, float* W, float* mom, int64_t n,
+                        const forge_sgdm_params* p, void* stream);
+
+/*
+ * Fused weight gradient + AdamW over E routed experts (grouped GEMM).
+ *   X_perm  [R, d_in]  bf16, dY_perm [R, d_out] bf16: the routed rows, grouped
+ *           by expert; expert e owns rows offsets[e] .. offsets[e+1]-1.
+ *   offsets HOST array of E+1 int64: offsets[0] == 0, non-decreasing,
+ *           R = offsets[E].
+ *   W, m, v [E, d_out, d_in] float32, contiguous, updated in place.
+ *   1 <= E <= FORGE_MAX_EXPERTS.
+ * Every expert takes step p->step, including experts with no rows: their
+ * gradient is exactly zero and their moments and weights still decay.
+ * FORGE assessment, "Math verified, not asserted", P5: an expert that
+ * receives no tokens runs no contraction, but skipping its optimizer step
+ * (or folding the decay into the contraction) is wrong for routed weights.
+ * Expert e's result is bitwise the dense call on its rows.
+ */
+FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void* dY_perm,
+                                       const int64_t* offsets, int32_t E,
+                                       float* W, float* m, float* v,
+                                       int64_t d_in, int64_t d_out,
+                                       const forge_adamw_params* p, forge_tile tile, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+FORGE_API const char* forge_status_string(forge_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FORGE_H */

@@ -1,0 +1,100 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the library on
+one side and the oracle on the other, and judge each step."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from oracle import judge
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def bf16_dev(bits: np.ndarray):
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to("cuda").view(torch.bfloat16)
+
+
+def f32_dev(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+def host(t, rows=None) -> np.ndarray:
+    if rows is not None:
+        idx = torch_mod().as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+        t = t.index_select(t.dim() - 2, idx)
+    return t.detach().cpu().numpy()
+
+
+def sample_rows(d_out: int, bn: int = 128, per_tile: int = 2, extra: int = 16, seed: int = 0):
+    """Rows of W spread over every 128-row block (first/last of each block,
+    plus random ones)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b0 in range(0, d_out, bn):
+        b1 = min(d_out, b0 + bn)
+        rows.add(b0)
+        rows.add(b1 - 1)
+        for r in rng.integers(b0, b1, size=max(0, per_tile - 2)):
+            rows.add(int(r))
+    for r in rng.integers(0, d_out, size=extra):
+        rows.add(int(r))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+class AdamWParity:
+    """Runs AdamW steps on the GPU state and on an oracle copy of (sampled rows
+    of) the state, judging every step."""
+
+    def __init__(self, W0, m0, v0, hp, rows=None, lead=None):
+        self.hp = dict(hp)
+        self.rows = rows
+        sel = (lambda a: a) if rows is None else (lambda a: a[..., rows, :])
+        self.Wr, self.mr, self.vr = sel(W0).copy(), sel(m0).copy(), sel(v0).copy()
+        self.floor = oracle.StateFloor(self.Wr.shape, "adamw", hp["beta1"], hp["beta2"])
+
+    def step(self, t, g_ref, tau, W_prev_gpu, W_gpu, m_gpu, v_gpu):
+        self.floor.update(tau, g_ref)
+        Wr_new, mr, vr = oracle.adamw_step(self.Wr, self.mr, self.vr, g_ref, t, **self.hp)
+        rep = judge.judge_adamw(t, W_prev_gpu, W_gpu, m_gpu, v_gpu, self.Wr, Wr_new, mr, vr,
+                                g_ref, tau, self.floor, **self.hp)
+        self.Wr, self.mr, self.vr = Wr_new, mr, vr
+        return rep
+
+
+class SgdmParity:
+    def __init__(self, W0, b0, hp, rows=None):
+        self.hp = dict(hp)
+        self.rows = rows
+        sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+        self.Wr, self.br = sel(W0).copy(), sel(b0).copy()
+        self.floor = oracle.StateFloor(self.Wr.shape, "sgdm", momentum=hp["momentum"])
+
+    def step(self, g_ref, tau, W_prev_gpu, W_gpu, b_gpu):
+        self.floor.update(tau, g_ref)
+        Wr_new, br = oracle.sgdm_step(self.Wr, self.br, g_ref, **self.hp)
+        rep = judge.judge_sgdm(W_prev_gpu, W_gpu, b_gpu, self.Wr, Wr_new, br, self.floor,
+                               self.hp["lr"])
+        self.Wr, self.br = Wr_new, br
+        return rep
+
+
+def adamw_hp(case):
+    return dict(lr=case.lr, beta1=case.beta1, beta2=case.beta2, eps=case.eps,
+                weight_decay=case.weight_decay)
+
+
+def bits_equal(a, b) -> bool:
+    return judge.bitwise_equal(a, b)

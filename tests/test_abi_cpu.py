@@ -1,0 +1,174 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments with the documented status codes before
+touching any buffer. Fake, never-dereferenced pointers are used throughout;
+the one case that passes validation is only run where no GPU is visible.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from weight_gradient_gemm_amd import _lib
+
+NULL = None
+A = 0x100000          # fake, 16-byte aligned "device" addresses far apart
+B = 0x200000000
+C = 0x400000000
+D = 0x600000000
+X_ADDR = 0x800000000
+Y_ADDR = 0xA00000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.library()
+
+
+def declared_symbols(root):
+    with open(os.path.join(root, "include", "forge.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"FORGE_API\s+[\w\s\*]*?\b(forge_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib, root):
+    names = declared_symbols(root)
+    assert names == sorted(["forge_adamw", "forge_grouped_wgrad_adamw", "forge_sgdm",
+                            "forge_status_string", "forge_wgrad", "forge_wgrad_adamw",
+                            "forge_wgrad_sgdm"])
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (forge_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings(lib):
+    for s in range(-1, 11):
+        txt = _lib.forge_status_string(s)
+        assert isinstance(txt, str) and txt
+    assert "clipping" in _lib.forge_status_string(6)
+
+
+def adam(**kw):
+    base = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1,
+                max_grad_norm=0.0)
+    base.update(kw)
+    return _lib.AdamWParams(base["lr"], base["beta1"], base["beta2"], base["eps"],
+                            base["weight_decay"], base["step"], base["max_grad_norm"])
+
+
+def sgd(**kw):
+    base = dict(lr=1e-3, momentum=0.9, weight_decay=0.0, max_grad_norm=0.0)
+    base.update(kw)
+    return _lib.SgdmParams(base["lr"], base["momentum"], base["weight_decay"],
+                           base["max_grad_norm"])
+
+
+def call_adamw(lib, X=X_ADDR, dY=Y_ADDR, W=A, m=B, v=C, T=64, d_in=64, d_out=32, p=None,
+               tile=0):
+    p = adam() if p is None else p
+    return lib.forge_wgrad_adamw(X, dY, W, m, v, T, d_in, d_out, ctypes.byref(p), tile, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=NULL), 1), (dict(m=NULL), 1), (dict(v=NULL), 1), (dict(X=NULL), 1), (dict(dY=NULL), 1),
+    (dict(T=-1), 2), (dict(d_in=-8), 2), (dict(d_out=-8), 2), (dict(T=1 << 31), 2),
+    (dict(d_in=12), 3), (dict(d_out=20), 3), (dict(W=A + 4), 3), (dict(X=X_ADDR + 2), 3),
+    (dict(dY=Y_ADDR + 8), 3),
+    (dict(m=A), 4), (dict(v=A + 64), 4), (dict(W=X_ADDR), 4), (dict(m=Y_ADDR - 16), 4),
+    (dict(p=adam(max_grad_norm=1.0)), 6), (dict(p=adam(max_grad_norm=float("inf"))), 6),
+    (dict(p=adam(max_grad_norm=-1.0)), 5), (dict(p=adam(max_grad_norm=float("nan"))), 5),
+    (dict(p=adam(beta1=1.0)), 5), (dict(p=adam(beta2=-0.1)), 5), (dict(p=adam(lr=-1e-3)), 5),
+    (dict(p=adam(eps=float("nan"))), 5), (dict(p=adam(step=0)), 5),
+    (dict(p=adam(weight_decay=float("inf"))), 5),
+    (dict(tile=3), 7), (dict(tile=-1), 7),
+])
+def test_wgrad_adamw_rejects(lib, kw, status):
+    assert call_adamw(lib, **kw) == status
+
+
+def test_clip_request_beats_other_hparam_errors(lib):
+    # fail closed on clipping even when another hyperparameter is also off
+    assert call_adamw(lib, p=adam(max_grad_norm=0.5, beta1=2.0)) == 6
+
+
+def test_empty_outputs_are_noops(lib):
+    # nothing to update: OK without a device (no launch, nothing touched)
+    assert call_adamw(lib, d_in=0) == 0
+    assert call_adamw(lib, d_out=0, W=NULL, m=NULL, v=NULL) == 0
+    assert lib.forge_adamw(A, B, C, D, 0, ctypes.byref(adam()), None) == 0
+
+
+def test_no_gpu_means_device_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: valid fake pointers would launch a kernel")
+    assert call_adamw(lib) == 8
+    assert call_adamw(lib, T=0, X=NULL, dY=NULL) == 8
+    p = sgd()
+    assert lib.forge_wgrad_sgdm(X_ADDR, Y_ADDR, A, B, 64, 64, 32, ctypes.byref(p), 0, None) == 8
+    assert lib.forge_wgrad(X_ADDR, Y_ADDR, A, 64, 64, 32, 0, None) == 8
+    assert lib.forge_adamw(A, B, C, D, 100, ctypes.byref(adam()), None) == 8
+    assert lib.forge_sgdm(A, B, C, 100, ctypes.byref(sgd()), None) == 8
+    offs = (ctypes.c_int64 * 3)(0, 10, 10)
+    assert lib.forge_grouped_wgrad_adamw(X_ADDR, Y_ADDR, offs, 2, A, B, C, 64, 32,
+                                         ctypes.byref(adam()), 0, None) == 8
+
+
+def test_sgdm_and_unfused_reject(lib):
+    p = sgd(momentum=1.0)
+    assert lib.forge_wgrad_sgdm(X_ADDR, Y_ADDR, A, B, 64, 64, 32, ctypes.byref(p), 0, None) == 5
+    p = sgd(max_grad_norm=2.0)
+    assert lib.forge_wgrad_sgdm(X_ADDR, Y_ADDR, A, B, 64, 64, 32, ctypes.byref(p), 0, None) == 6
+    assert lib.forge_wgrad_sgdm(X_ADDR, Y_ADDR, A, A, 64, 64, 32, ctypes.byref(sgd()), 0,
+                                None) == 4
+    assert lib.forge_wgrad(X_ADDR, Y_ADDR, NULL, 64, 64, 32, 0, None) == 1
+    assert lib.forge_wgrad(X_ADDR, Y_ADDR, X_ADDR + 64, 64, 64, 32, 0, None) == 4
+    assert lib.forge_adamw(A, B, C, D, -1, ctypes.byref(adam()), None) == 2
+    assert lib.forge_adamw(A, A, C, D, 100, ctypes.byref(adam()), None) == 4
+    assert lib.forge_adamw(A + 4, B, C, D, 100, ctypes.byref(adam()), None) == 3
+    assert lib.forge_adamw(A, B, C, D, 100, None, None) == 1
+    assert lib.forge_sgdm(A, B, NULL, 100, ctypes.byref(sgd()), None) == 1
+
+
+def test_grouped_rejects(lib):
+    def call(offs, E=None, W=A, m=B, v=C, d_in=64, d_out=32, p=None):
+        E = len(offs) - 1 if E is None else E
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        p = adam() if p is None else p
+        return lib.forge_grouped_wgrad_adamw(X_ADDR, Y_ADDR, arr, E, W, m, v, d_in, d_out,
+                                             ctypes.byref(p), 0, None)
+
+    assert lib.forge_grouped_wgrad_adamw(X_ADDR, Y_ADDR, None, 2, A, B, C, 64, 32,
+                                         ctypes.byref(adam()), 0, None) == 1
+    assert call([0], E=0) == 2
+    assert call([0] * 258, E=257) == 2
+    assert call([1, 4, 9]) == 2                  # offsets[0] != 0
+    assert call([0, 9, 4]) == 2                  # decreasing
+    assert call([0, 4, 9], d_in=36) == 3
+    assert call([0, 4, 9], m=A + 64 * 32 * 4) == 4   # m overlaps expert 1 of W
+    assert call([0, 4, 9], p=adam(max_grad_norm=1.0)) == 6
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "library_path", str(tmp_path / "libforge.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.library()
+
+
+def test_kernel_sources_have_no_atomics_or_split_k(root):
+    # no atomics anywhere in the device code (order of accumulation is fixed)
+    csrc = os.path.join(root, "weight_gradient_gemm_amd", "csrc")
+    for fn in os.listdir(csrc):
+        with open(os.path.join(csrc, fn)) as f:
+            text = f.read()
+        code = re.sub(r"//.*", "", text)
+        assert not re.search(r"atomic(Add|Max|Min|CAS|Exch|_)", code, re.I) or fn == "forge.hip", fn
+        assert not re.search(r"split_?k", code, re.I), fn
+    with open(os.path.join(csrc, "wgrad_kernels.hpp")) as f:
+        kern = re.sub(r"//.*", "", f.read())
+    assert "atomic" not in kern.lower()

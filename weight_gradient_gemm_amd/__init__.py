@@ -1,0 +1,24 @@
+"""Fused weight-gradient GEMM + optimizer step for AMD MI355X (gfx950).
+
+A thin binding over the C ABI in include/forge.h (libforge.so, built in-tree by
+``python -m weight_gradient_gemm_amd.build``). Every step of the path runs in
+the library's HIP kernels; this module only turns torch tensors into device
+pointers and sizes and passes the current HIP stream. There is no CPU path:
+if the library is missing, importing the entry points raises.
+"""
+from ._lib import (  # noqa: F401
+    FORGE_TILE_128x128,
+    FORGE_TILE_256x128,
+    FORGE_TILE_DEFAULT,
+    ForgeError,
+    STATUS,
+    forge_adamw,
+    forge_grouped_wgrad_adamw,
+    forge_sgdm,
+    forge_status_string,
+    forge_wgrad,
+    forge_wgrad_adamw,
+    forge_wgrad_sgdm,
+    library,
+    library_path,
+)

@@ -1,0 +1,246 @@
+"""ctypes binding of libforge.so; argument marshalling only.
+
+Each Python function has the name of the C entry point it calls and takes
+torch tensors: bf16 X / dY, float32 W and optimizer state, all contiguous on
+the current HIP device. Sizes are read off the tensors; the library validates
+everything else and its status code is raised as ForgeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(PKG, "libforge.so")
+
+FORGE_TILE_DEFAULT = 0
+FORGE_TILE_256x128 = 1
+FORGE_TILE_128x128 = 2
+
+STATUS = {
+    0: "FORGE_OK", 1: "FORGE_ERR_NULL", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_ALIGN",
+    4: "FORGE_ERR_ALIAS", 5: "FORGE_ERR_HPARAM", 6: "FORGE_ERR_CLIP_NOT_FUSABLE",
+    7: "FORGE_ERR_TILE", 8: "FORGE_ERR_DEVICE", 9: "FORGE_ERR_LAUNCH",
+}
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class AdamWParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", _i64),
+                ("max_grad_norm", ctypes.c_double)]
+
+
+class SgdmParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("max_grad_norm", ctypes.c_double)]
+
+
+class ForgeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        self.name = STATUS.get(self.status, str(status))
+        super().__init__(f"{where}: {self.name} ({forge_status_string(self.status)})")
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libforge.so. Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m weight_gradient_gemm_amd.build` (needs hipcc)")
+        lib = ctypes.CDLL(library_path)
+        lib.forge_wgrad_adamw.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                          ctypes.POINTER(AdamWParams), _i32, _vp]
+        lib.forge_wgrad_sgdm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                         ctypes.POINTER(SgdmParams), _i32, _vp]
+        lib.forge_wgrad.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
+        lib.forge_adamw.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(AdamWParams), _vp]
+        lib.forge_sgdm.argtypes = [_vp, _vp, _vp, _i64, ctypes.POINTER(SgdmParams), _vp]
+        lib.forge_grouped_wgrad_adamw.argtypes = [_vp, _vp, ctypes.POINTER(_i64), _i32, _vp, _vp,
+                                                  _vp, _i64, _i64, ctypes.POINTER(AdamWParams),
+                                                  _i32, _vp]
+        lib.forge_status_string.argtypes = [_i32]
+        lib.forge_status_string.restype = ctypes.c_char_p
+        for name in ("forge_wgrad_adamw", "forge_wgrad_sgdm", "forge_wgrad", "forge_adamw",
+                     "forge_sgdm", "forge_grouped_wgrad_adamw"):
+            getattr(lib, name).restype = _i32
+        _LIB = lib
+    return _LIB
+
+
+def forge_status_string(status: int) -> str:
+    return library().forge_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise ForgeError(status, where)
+
+
+# --------------------------------------------------------------------------
+# tensor marshalling
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _want(t, dtype, name):
+    if t is None:
+        return
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape2(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm):
+    return AdamWParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                       int(step), float(max_grad_norm))
+
+
+def _state_like(W, others, d_out, d_in, lead=()):
+    want = (*lead, d_out, d_in)
+    for name, t in (("W", W), *others):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+        _want(t, _torch().float32, name)
+
+
+# --------------------------------------------------------------------------
+# entry points (names as in include/forge.h)
+# --------------------------------------------------------------------------
+def forge_wgrad_adamw(X, dY, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                      weight_decay=0.01, max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT,
+                      stream=None) -> None:
+    """W, m, v <- AdamW(W, m, v, g = dY^T X), in place, g never stored."""
+    torch = _torch()
+    _want(X, torch.bfloat16, "X")
+    _want(dY, torch.bfloat16, "dY")
+    T, d_in = _shape2(X, "X")
+    T2, d_out = _shape2(dY, "dY")
+    if T2 != T:
+        raise ValueError(f"X has {T} token rows, dY has {T2}")
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in)
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_wgrad_adamw(_ptr(X), _ptr(dY), _ptr(W), _ptr(m), _ptr(v), T, d_in,
+                                       d_out, ctypes.byref(p), int(tile), _stream(stream)),
+           "forge_wgrad_adamw")
+
+
+def forge_wgrad_sgdm(X, dY, W, mom, *, lr=1e-3, momentum=0.9, weight_decay=0.0,
+                     max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """W, mom <- SGD-momentum(W, mom, g = dY^T X), in place, g never stored."""
+    torch = _torch()
+    _want(X, torch.bfloat16, "X")
+    _want(dY, torch.bfloat16, "dY")
+    T, d_in = _shape2(X, "X")
+    T2, d_out = _shape2(dY, "dY")
+    if T2 != T:
+        raise ValueError(f"X has {T} token rows, dY has {T2}")
+    _state_like(W, (("mom", mom),), d_out, d_in)
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_wgrad_sgdm(_ptr(X), _ptr(dY), _ptr(W), _ptr(mom), T, d_in, d_out,
+                                      ctypes.byref(p), int(tile), _stream(stream)),
+           "forge_wgrad_sgdm")
+
+
+def forge_wgrad(X, dY, grad, *, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """grad <- dY^T X in float32 (the unfused comparison path)."""
+    torch = _torch()
+    _want(X, torch.bfloat16, "X")
+    _want(dY, torch.bfloat16, "dY")
+    T, d_in = _shape2(X, "X")
+    T2, d_out = _shape2(dY, "dY")
+    if T2 != T:
+        raise ValueError(f"X has {T} token rows, dY has {T2}")
+    _state_like(grad, (), d_out, d_in)
+    _check(library().forge_wgrad(_ptr(X), _ptr(dY), _ptr(grad), T, d_in, d_out, int(tile),
+                                 _stream(stream)), "forge_wgrad")
+
+
+def forge_adamw(grad, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                weight_decay=0.01, max_grad_norm=0.0, stream=None) -> None:
+    """Elementwise AdamW from a stored float32 gradient (unfused path)."""
+    torch = _torch()
+    for name, t in (("grad", grad), ("W", W), ("m", m), ("v", v)):
+        _want(t, torch.float32, name)
+        if t.numel() != grad.numel():
+            raise ValueError(f"{name} has {t.numel()} elements, grad has {grad.numel()}")
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_adamw(_ptr(grad), _ptr(W), _ptr(m), _ptr(v), grad.numel(),
+                                 ctypes.byref(p), _stream(stream)), "forge_adamw")
+
+
+def forge_sgdm(grad, W, mom, *, lr=1e-3, momentum=0.9, weight_decay=0.0, max_grad_norm=0.0,
+               stream=None) -> None:
+    """Elementwise SGD-momentum from a stored float32 gradient (unfused path)."""
+    torch = _torch()
+    for name, t in (("grad", grad), ("W", W), ("mom", mom)):
+        _want(t, torch.float32, name)
+        if t.numel() != grad.numel():
+            raise ValueError(f"{name} has {t.numel()} elements, grad has {grad.numel()}")
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_sgdm(_ptr(grad), _ptr(W), _ptr(mom), grad.numel(), ctypes.byref(p),
+                                _stream(stream)), "forge_sgdm")
+
+
+def forge_grouped_wgrad_adamw(X_perm, dY_perm, offsets, W, m, v, *, step, lr=1e-3, beta1=0.9,
+                              beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                              tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """AdamW on E routed experts; expert e contracts rows offsets[e]:offsets[e+1].
+
+    ``offsets`` is a host sequence of E+1 ints. Experts with no rows still
+    take the step (zero gradient)."""
+    torch = _torch()
+    _want(X_perm, torch.bfloat16, "X_perm")
+    _want(dY_perm, torch.bfloat16, "dY_perm")
+    R, d_in = _shape2(X_perm, "X_perm")
+    R2, d_out = _shape2(dY_perm, "dY_perm")
+    if R2 != R:
+        raise ValueError(f"X_perm has {R} rows, dY_perm has {R2}")
+    offs = [int(x) for x in offsets]
+    E = len(offs) - 1
+    if E < 1:
+        raise ValueError("offsets must hold E+1 >= 2 entries")
+    if offs[-1] != R:
+        raise ValueError(f"offsets[E] = {offs[-1]} but X_perm has {R} rows")
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in, lead=(E,))
+    arr = (_i64 * (E + 1))(*offs)
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_grouped_wgrad_adamw(_ptr(X_perm), _ptr(dY_perm), arr, E, _ptr(W),
+                                               _ptr(m), _ptr(v), d_in, d_out, ctypes.byref(p),
+                                               int(tile), _stream(stream)),
+           "forge_grouped_wgrad_adamw")

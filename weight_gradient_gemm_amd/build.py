@@ -1,0 +1,62 @@
+"""Builds libforge.so in-tree for gfx950.
+
+    python -m weight_gradient_gemm_amd.build
+
+The host-only validation is compiled with g++; the HIP translation unit with
+hipcc. Floating-point flags are pinned: no contraction of multiply-add pairs
+(the optimizer arithmetic is rounded exactly as written), IEEE-rounded float32
+division and square root, and no packed-fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libforge.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra"]
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libforge.so")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libforge.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    v_obj = os.path.join(BUILD, "validate.o")
+    h_obj = os.path.join(BUILD, "forge.o")
+    _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "validate.cpp"), "-o", v_obj], verbose)
+    _run([_hipcc(), *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "forge.hip"), "-o", h_obj], verbose)
+    tmp = LIB + ".tmp"
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", h_obj, v_obj, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

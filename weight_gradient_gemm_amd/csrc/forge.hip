@@ -1,0 +1,260 @@
+// Host side of the forge C ABI: validation, per-step scalars, tile choice and
+// kernel launch on the caller's stream. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "forge.h"
+#include "validate.hpp"
+#include "wgrad_kernels.hpp"
+
+namespace forge {
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device verdict of the architecture check: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+forge_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FORGE_ERR_DEVICE;
+  }
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FORGE_ERR_DEVICE;
+    }
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? FORGE_OK : FORGE_ERR_DEVICE;
+}
+
+AdamWConsts make_adamw(const forge_adamw_params& p) {
+  const double t = double(p.step);
+  const double bc1 = 1.0 - std::pow(p.beta1, t);
+  const double bc2 = 1.0 - std::pow(p.beta2, t);
+  AdamWConsts c;
+  c.beta1 = float(p.beta1);
+  c.one_m_beta1 = float(1.0 - p.beta1);
+  c.beta2 = float(p.beta2);
+  c.one_m_beta2 = float(1.0 - p.beta2);
+  c.decay = float(1.0 - p.lr * p.weight_decay);
+  c.step_size = float(p.lr / bc1);
+  c.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+  c.eps = float(p.eps);
+  return c;
+}
+
+SgdmConsts make_sgdm(const forge_sgdm_params& p) {
+  SgdmConsts c;
+  c.momentum = float(p.momentum);
+  c.weight_decay = float(p.weight_decay);
+  c.lr = float(p.lr);
+  return c;
+}
+
+struct TileShape {
+  int bm, bn;
+};
+
+TileShape shape_of(forge_tile t) {
+  switch (t) {
+    case FORGE_TILE_128x128: return {128, 128};
+    case FORGE_TILE_256x128:
+    default: return {256, 128};
+  }
+}
+
+int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s) {
+  return ((d_in + s.bm - 1) / s.bm) * ((d_out + s.bn - 1) / s.bn);
+}
+
+// Default tile: the large tile unless it leaves most compute units idle.
+forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts) {
+  if (t != FORGE_TILE_DEFAULT) return t;
+  if (experts * count_tiles(d_in, d_out, shape_of(FORGE_TILE_256x128)) < 256)
+    return FORGE_TILE_128x128;
+  return FORGE_TILE_256x128;
+}
+
+forge_status launch_status() {
+  return hipGetLastError() == hipSuccess ? FORGE_OK : FORGE_ERR_LAUNCH;
+}
+
+template <int BM, int BN, int EPI>
+forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
+  a.tiles_m = int32_t((a.d_in + BM - 1) / BM);
+  a.tiles_n = int32_t((a.d_out + BN - 1) / BN);
+  a.num_tiles = a.tiles_m * a.tiles_n;
+  a.group_m = 4;
+  hipLaunchKernelGGL((wgrad_dense_kernel<BM, BN, 2, EPI>), dim3(a.num_tiles), dim3(kThreads), 0,
+                     s, a);
+  return launch_status();
+}
+
+template <int EPI>
+forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
+  switch (tile) {
+    case FORGE_TILE_128x128: return launch_dense_t<128, 128, EPI>(a, s);
+    case FORGE_TILE_256x128: return launch_dense_t<256, 128, EPI>(a, s);
+    default: return FORGE_ERR_TILE;
+  }
+}
+
+template <int BM, int BN>
+forge_status launch_grouped_t(WgradArgs a, const GroupTable& gt, int32_t E, hipStream_t s) {
+  a.tiles_m = int32_t((a.d_in + BM - 1) / BM);
+  a.tiles_n = int32_t((a.d_out + BN - 1) / BN);
+  a.num_tiles = a.tiles_m * a.tiles_n * E;
+  a.group_m = 4;
+  hipLaunchKernelGGL((wgrad_grouped_kernel<BM, BN, 2, EPI_ADAMW>), dim3(a.num_tiles),
+                     dim3(kThreads), 0, s, a, gt);
+  return launch_status();
+}
+
+WgradArgs base_args(const void* X, const void* dY, float* W, float* S1, float* S2, int64_t T,
+                    int64_t d_in, int64_t d_out) {
+  WgradArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = static_cast<const uint16_t*>(X);
+  a.dY = static_cast<const uint16_t*>(dY);
+  a.W = W;
+  a.S1 = S1;
+  a.S2 = S2;
+  a.T = T;
+  a.d_in = int32_t(d_in);
+  a.d_out = int32_t(d_out);
+  return a;
+}
+
+// Tile counts must fit the kernels' 32-bit block indices.
+bool grid_fits(int64_t d_in, int64_t d_out, forge_tile tile, int64_t experts) {
+  return experts * count_tiles(d_in, d_out, shape_of(tile)) < (int64_t(1) << 31);
+}
+
+}  // namespace
+}  // namespace forge
+
+using namespace forge;
+
+extern "C" {
+
+FORGE_API forge_status forge_wgrad_adamw(const void* X, const void* dY, float* W, float* m,
+                                         float* v, int64_t T, int64_t d_in, int64_t d_out,
+                                         const forge_adamw_params* p, forge_tile tile,
+                                         void* stream) {
+  if (forge_status s = validate_wgrad_adamw(X, dY, W, m, v, T, d_in, d_out, p, tile)) return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, W, m, v, T, d_in, d_out);
+  a.adam = make_adamw(*p);
+  return launch_dense<EPI_ADAMW>(a, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_wgrad_sgdm(const void* X, const void* dY, float* W, float* mom,
+                                        int64_t T, int64_t d_in, int64_t d_out,
+                                        const forge_sgdm_params* p, forge_tile tile,
+                                        void* stream) {
+  if (forge_status s = validate_wgrad_sgdm(X, dY, W, mom, T, d_in, d_out, p, tile)) return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, W, mom, nullptr, T, d_in, d_out);
+  a.sgd = make_sgdm(*p);
+  return launch_dense<EPI_SGDM>(a, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_wgrad(const void* X, const void* dY, float* grad, int64_t T,
+                                   int64_t d_in, int64_t d_out, forge_tile tile, void* stream) {
+  if (forge_status s = validate_wgrad(X, dY, grad, T, d_in, d_out, tile)) return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, grad, nullptr, nullptr, T, d_in, d_out);
+  return launch_dense<EPI_GRAD>(a, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_adamw(const float* grad, float* W, float* m, float* v, int64_t n,
+                                   const forge_adamw_params* p, void* stream) {
+  if (forge_status s = validate_adamw(grad, W, m, v, n, p)) return s;
+  if (n == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  const int64_t n4 = (n + 3) / 4;
+  const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
+  hipLaunchKernelGGL(adamw_elementwise_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), grad, W, m, v, n, make_adamw(*p));
+  return launch_status();
+}
+
+FORGE_API forge_status forge_sgdm(const float* grad, float* W, float* mom, int64_t n,
+                                  const forge_sgdm_params* p, void* stream) {
+  if (forge_status s = validate_sgdm(grad, W, mom, n, p)) return s;
+  if (n == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  const int64_t n4 = (n + 3) / 4;
+  const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
+  hipLaunchKernelGGL(sgdm_elementwise_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), grad, W, mom, n, make_sgdm(*p));
+  return launch_status();
+}
+
+FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void* dY_perm,
+                                                 const int64_t* offsets, int32_t E, float* W,
+                                                 float* m, float* v, int64_t d_in, int64_t d_out,
+                                                 const forge_adamw_params* p, forge_tile tile,
+                                                 void* stream) {
+  if (forge_status s = validate_grouped_adamw(X_perm, dY_perm, offsets, E, W, m, v, d_in, d_out,
+                                              p, tile))
+    return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  tile = resolve_tile(tile, d_in, d_out, E);
+  if (!grid_fits(d_in, d_out, tile, E)) return FORGE_ERR_SHAPE;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  GroupTable gt;
+  std::memset(&gt, 0, sizeof(gt));
+  for (int32_t e = 0; e <= E; ++e) gt.off[e] = offsets[e];
+  WgradArgs a = base_args(X_perm, dY_perm, W, m, v, 0, d_in, d_out);
+  a.adam = make_adamw(*p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (tile) {
+    case FORGE_TILE_128x128: return launch_grouped_t<128, 128>(a, gt, E, s);
+    case FORGE_TILE_256x128: return launch_grouped_t<256, 128>(a, gt, E, s);
+    default: return FORGE_ERR_TILE;
+  }
+}
+
+FORGE_API const char* forge_status_string(forge_status s) {
+  switch (s) {
+    case FORGE_OK: return "ok";
+    case FORGE_ERR_NULL: return "a required pointer is NULL";
+    case FORGE_ERR_SHAPE: return "invalid or unsupported size";
+    case FORGE_ERR_ALIGN: return "pointer not 16-byte aligned, or d_in/d_out not a multiple of 8";
+    case FORGE_ERR_ALIAS: return "output buffers overlap each other or an input";
+    case FORGE_ERR_HPARAM: return "hyperparameter out of range";
+    case FORGE_ERR_CLIP_NOT_FUSABLE:
+      return "global-norm clipping cannot be fused into the weight-gradient epilogue";
+    case FORGE_ERR_TILE: return "unknown tile id";
+    case FORGE_ERR_DEVICE: return "no gfx950 device is current";
+    case FORGE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

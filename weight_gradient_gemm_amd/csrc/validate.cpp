@@ -1,0 +1,201 @@
+// Host-side argument validation for the forge C ABI (pure C++, no HIP).
+#include "validate.hpp"
+
+#include <cmath>
+
+namespace forge {
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
+
+// Rejects NaN as well as anything outside [0, 1).
+bool unit_interval(double x) { return x >= 0.0 && x < 1.0; }
+
+forge_status check_clip(double max_grad_norm) {
+  if (std::isnan(max_grad_norm) || max_grad_norm < 0.0) return FORGE_ERR_HPARAM;
+  if (max_grad_norm > 0.0) return FORGE_ERR_CLIP_NOT_FUSABLE;
+  return FORGE_OK;
+}
+
+forge_status check_outs_disjoint(const Span* spans, int n) {
+  for (int a = 0; a < n; ++a)
+    for (int b = a + 1; b < n; ++b)
+      if (spans_overlap(spans[a], spans[b])) return FORGE_ERR_ALIAS;
+  return FORGE_OK;
+}
+
+}  // namespace
+
+bool spans_overlap(const Span& a, const Span& b) {
+  if (a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+forge_status check_tile(forge_tile tile) {
+  return (tile >= 0 && tile < FORGE_TILE_COUNT) ? FORGE_OK : FORGE_ERR_TILE;
+}
+
+forge_status check_dense(const void* X, const void* dY, const void* const* outs, int n_outs,
+                         int64_t T, int64_t d_in, int64_t d_out) {
+  if (T < 0 || d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
+  const bool empty_out = d_in == 0 || d_out == 0;
+  if (!empty_out) {
+    for (int k = 0; k < n_outs; ++k)
+      if (!outs[k]) return FORGE_ERR_NULL;
+    if (T > 0 && (!X || !dY)) return FORGE_ERR_NULL;
+  }
+  if (T > kMaxTokens || d_in > kMaxDim || d_out > kMaxDim) return FORGE_ERR_SHAPE;
+  if (d_in * d_out > kMaxElems) return FORGE_ERR_SHAPE;
+  if (empty_out) return FORGE_OK;
+  if ((d_in % 8) != 0 || (d_out % 8) != 0) return FORGE_ERR_ALIGN;
+  for (int k = 0; k < n_outs; ++k)
+    if (!aligned16(outs[k])) return FORGE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(X) || !aligned16(dY))) return FORGE_ERR_ALIGN;
+
+  Span spans[6] = {};
+  int n = 0;
+  const uint64_t state_bytes = uint64_t(d_in) * uint64_t(d_out) * 4u;
+  for (int k = 0; k < n_outs; ++k) spans[n++] = Span{outs[k], state_bytes};
+  if (forge_status s = check_outs_disjoint(spans, n)) return s;
+  if (T > 0) {
+    const Span sx{X, uint64_t(T) * uint64_t(d_in) * 2u}, sy{dY, uint64_t(T) * uint64_t(d_out) * 2u};
+    for (int k = 0; k < n_outs; ++k)
+      if (spans_overlap(spans[k], sx) || spans_overlap(spans[k], sy)) return FORGE_ERR_ALIAS;
+  }
+  return FORGE_OK;
+}
+
+forge_status check_adamw_params(const forge_adamw_params* p) {
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_clip(p->max_grad_norm)) return s;
+  if (!finite_nonneg(p->lr) || !unit_interval(p->beta1) || !unit_interval(p->beta2) ||
+      !finite_nonneg(p->eps) || !finite_nonneg(p->weight_decay) || p->step < 1)
+    return FORGE_ERR_HPARAM;
+  return FORGE_OK;
+}
+
+forge_status check_sgdm_params(const forge_sgdm_params* p) {
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_clip(p->max_grad_norm)) return s;
+  if (!finite_nonneg(p->lr) || !unit_interval(p->momentum) || !finite_nonneg(p->weight_decay))
+    return FORGE_ERR_HPARAM;
+  return FORGE_OK;
+}
+
+forge_status check_elementwise(const float* grad, const float* const* outs, int n_outs,
+                               int64_t n) {
+  if (n < 0) return FORGE_ERR_SHAPE;
+  if (n == 0) return FORGE_OK;
+  if (!grad) return FORGE_ERR_NULL;
+  for (int k = 0; k < n_outs; ++k)
+    if (!outs[k]) return FORGE_ERR_NULL;
+  if (n > kMaxElems) return FORGE_ERR_SHAPE;
+  if (!aligned16(grad)) return FORGE_ERR_ALIGN;
+  for (int k = 0; k < n_outs; ++k)
+    if (!aligned16(outs[k])) return FORGE_ERR_ALIGN;
+  Span spans[4] = {};
+  int m = 0;
+  for (int k = 0; k < n_outs; ++k) spans[m++] = Span{outs[k], uint64_t(n) * 4u};
+  if (forge_status s = check_outs_disjoint(spans, m)) return s;
+  const Span sg{grad, uint64_t(n) * 4u};
+  for (int k = 0; k < m; ++k)
+    if (spans_overlap(spans[k], sg)) return FORGE_ERR_ALIAS;
+  return FORGE_OK;
+}
+
+forge_status check_grouped(const void* X_perm, const void* dY_perm, const int64_t* offsets,
+                           int32_t E, const void* const* outs, int n_outs, int64_t d_in,
+                           int64_t d_out) {
+  if (!offsets) return FORGE_ERR_NULL;
+  if (E < 1 || E > FORGE_MAX_EXPERTS) return FORGE_ERR_SHAPE;
+  if (offsets[0] != 0) return FORGE_ERR_SHAPE;
+  for (int32_t e = 0; e < E; ++e)
+    if (offsets[e + 1] < offsets[e]) return FORGE_ERR_SHAPE;
+  const int64_t R = offsets[E];
+  if (d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
+  const bool empty_out = d_in == 0 || d_out == 0;
+  if (!empty_out) {
+    for (int k = 0; k < n_outs; ++k)
+      if (!outs[k]) return FORGE_ERR_NULL;
+    if (R > 0 && (!X_perm || !dY_perm)) return FORGE_ERR_NULL;
+  }
+  if (R > kMaxTokens || d_in > kMaxDim || d_out > kMaxDim) return FORGE_ERR_SHAPE;
+  if (d_in * d_out > kMaxElems / E) return FORGE_ERR_SHAPE;
+  if (empty_out) return FORGE_OK;
+  if ((d_in % 8) != 0 || (d_out % 8) != 0) return FORGE_ERR_ALIGN;
+  for (int k = 0; k < n_outs; ++k)
+    if (!aligned16(outs[k])) return FORGE_ERR_ALIGN;
+  if (R > 0 && (!aligned16(X_perm) || !aligned16(dY_perm))) return FORGE_ERR_ALIGN;
+  Span spans[4] = {};
+  int n = 0;
+  const uint64_t state_bytes = uint64_t(E) * uint64_t(d_in) * uint64_t(d_out) * 4u;
+  for (int k = 0; k < n_outs; ++k) spans[n++] = Span{outs[k], state_bytes};
+  if (forge_status s = check_outs_disjoint(spans, n)) return s;
+  if (R > 0) {
+    const Span sx{X_perm, uint64_t(R) * uint64_t(d_in) * 2u};
+    const Span sy{dY_perm, uint64_t(R) * uint64_t(d_out) * 2u};
+    for (int k = 0; k < n; ++k)
+      if (spans_overlap(spans[k], sx) || spans_overlap(spans[k], sy)) return FORGE_ERR_ALIAS;
+  }
+  return FORGE_OK;
+}
+
+forge_status validate_wgrad_adamw(const void* X, const void* dY, const float* W, const float* m,
+                                  const float* v, int64_t T, int64_t d_in, int64_t d_out,
+                                  const forge_adamw_params* p, forge_tile tile) {
+  const void* outs[3] = {W, m, v};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense(X, dY, outs, 3, T, d_in, d_out)) return s;
+  if (forge_status s = check_adamw_params(p)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_wgrad_sgdm(const void* X, const void* dY, const float* W, const float* mom,
+                                 int64_t T, int64_t d_in, int64_t d_out,
+                                 const forge_sgdm_params* p, forge_tile tile) {
+  const void* outs[2] = {W, mom};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense(X, dY, outs, 2, T, d_in, d_out)) return s;
+  if (forge_status s = check_sgdm_params(p)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_wgrad(const void* X, const void* dY, const float* grad, int64_t T,
+                            int64_t d_in, int64_t d_out, forge_tile tile) {
+  const void* outs[1] = {grad};
+  if (forge_status s = check_dense(X, dY, outs, 1, T, d_in, d_out)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_adamw(const float* grad, const float* W, const float* m, const float* v,
+                            int64_t n, const forge_adamw_params* p) {
+  const float* outs[3] = {W, m, v};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_elementwise(grad, outs, 3, n)) return s;
+  return check_adamw_params(p);
+}
+
+forge_status validate_sgdm(const float* grad, const float* W, const float* mom, int64_t n,
+                           const forge_sgdm_params* p) {
+  const float* outs[2] = {W, mom};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_elementwise(grad, outs, 2, n)) return s;
+  return check_sgdm_params(p);
+}
+
+forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
+                                    const int64_t* offsets, int32_t E, const float* W,
+                                    const float* m, const float* v, int64_t d_in, int64_t d_out,
+                                    const forge_adamw_params* p, forge_tile tile) {
+  const void* outs[3] = {W, m, v};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_grouped(X_perm, dY_perm, offsets, E, outs, 3, d_in, d_out)) return s;
+  if (forge_status s = check_adamw_params(p)) return s;
+  return check_tile(tile);
+}
+
+}  // namespace forge

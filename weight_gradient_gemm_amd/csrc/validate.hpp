@@ -1,0 +1,59 @@
+// Host-side argument validation for the forge C ABI. Pure C++: no HIP calls,
+// so every error path can be exercised on a machine without a GPU.
+//
+// Order of checks (the first failing one is returned): NULL, SHAPE, ALIGN,
+// ALIAS, CLIP_NOT_FUSABLE, HPARAM, TILE. The device check and the launch come
+// after validation, in the HIP translation unit.
+#pragma once
+
+#include <cstdint>
+
+#include "forge.h"
+
+namespace forge {
+
+struct Span {
+  const void* p;
+  uint64_t bytes;
+};
+
+// True if the two byte ranges overlap (empty ranges never overlap).
+bool spans_overlap(const Span& a, const Span& b);
+
+forge_status check_dense(const void* X, const void* dY, const void* const* outs, int n_outs,
+                         int64_t T, int64_t d_in, int64_t d_out);
+forge_status check_adamw_params(const forge_adamw_params* p);
+forge_status check_sgdm_params(const forge_sgdm_params* p);
+forge_status check_tile(forge_tile tile);
+forge_status check_elementwise(const float* grad, const float* const* outs, int n_outs, int64_t n);
+forge_status check_grouped(const void* X_perm, const void* dY_perm, const int64_t* offsets,
+                           int32_t E, const void* const* outs, int n_outs, int64_t d_in,
+                           int64_t d_out);
+
+// Full validation of each entry point, everything except the device.
+forge_status validate_wgrad_adamw(const void* X, const void* dY, const float* W, const float* m,
+                                  const float* v, int64_t T, int64_t d_in, int64_t d_out,
+                                  const forge_adamw_params* p, forge_tile tile);
+forge_status validate_wgrad_sgdm(const void* X, const void* dY, const float* W, const float* mom,
+                                 int64_t T, int64_t d_in, int64_t d_out,
+                                 const forge_sgdm_params* p, forge_tile tile);
+forge_status validate_wgrad(const void* X, const void* dY, const float* grad, int64_t T,
+                            int64_t d_in, int64_t d_out, forge_tile tile);
+forge_status validate_adamw(const float* grad, const float* W, const float* m, const float* v,
+                            int64_t n, const forge_adamw_params* p);
+forge_status validate_sgdm(const float* grad, const float* W, const float* mom, int64_t n,
+                           const forge_sgdm_params* p);
+forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
+                                    const int64_t* offsets, int32_t E, const float* W,
+                                    const float* m, const float* v, int64_t d_in, int64_t d_out,
+                                    const forge_adamw_params* p, forge_tile tile);
+
+// Largest d_in, d_out and token count the kernels index (32-bit row/column
+// indices, 64-bit element offsets).
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+// One buffer of the optimizer state, in elements (64-bit offsets; bounded so
+// byte counts never overflow).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+}  // namespace forge
