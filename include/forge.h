@@ -135,7 +135,8 @@ enum {
   FORGE_TILE_DEFAULT = 0,   /* library's choice for the shape                     */
   FORGE_TILE_256x128 = 1,
   FORGE_TILE_128x128 = 2,
-  FORGE_TILE_COUNT = 3
+  FORGE_TILE_256x256 = 3,
+  FORGE_TILE_COUNT = 4
 };
 
 /* Maximum number of experts in one grouped call. */

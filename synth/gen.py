@@ -199,11 +199,13 @@ def lmhead_dy(seed: int, T: int, V: int, support: int = LMHEAD_SUPPORT,
         tot = w.sum()
         p = w / tot if tot > 0 else np.full(support, 1.0 / support)
         p[p < LMHEAD_FLOOR] = 0.0
-        row = np.zeros(V, dtype=np.float64)
-        row[ids] = p
-        row[labels[t]] -= 1.0
-        nz = np.nonzero(row)[0]
-        out[t, nz] = bf16_bits_from_f32(row[nz].astype(np.float32))
+        hit = np.nonzero(ids == labels[t])[0]
+        if hit.size:
+            p[hit[0]] -= 1.0
+        else:
+            ids = np.append(ids, labels[t])
+            p = np.append(p, -1.0)
+        out[t, ids] = bf16_bits_from_f32(p.astype(np.float32))
     return out
 
 

@@ -7,6 +7,7 @@ import sys
 import numpy as np
 
 import oracle
+import synth
 from oracle import judge
 
 
@@ -98,3 +99,47 @@ def adamw_hp(case):
 
 def bits_equal(a, b) -> bool:
     return judge.bitwise_equal(a, b)
+
+
+def run_dense_adamw(wg, case, steps, tile=0, rows=None):
+    """AdamW steps of `case` on the GPU, judged against the oracle each step."""
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, adamw_hp(case), rows=rows)
+    for t in range(1, steps + 1):
+        log(f"[{case.name}] adamw step {t} tile {tile}")
+        Xb, dYb = synth.dense_inputs(case, t)
+        W_prev = host(W, rows)
+        wg.forge_wgrad_adamw(bf16_dev(Xb), bf16_dev(dYb), W, m, v, step=t, tile=tile,
+                             **adamw_hp(case))
+        torch_mod().cuda.synchronize()
+        if rows is None:
+            g_ref, tau = oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb)
+        else:
+            g_ref, tau = oracle.wgrad_rows(Xb, dYb, rows), oracle.acc_floor_rows(Xb, dYb, rows)
+        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+    return W, m, v
+
+
+def run_dense_sgdm(wg, case, steps, tile=0, rows=None, weight_decay=0.0):
+    W0, _, _ = synth.dense_state(case)
+    b0 = np.zeros_like(W0)
+    W, b = f32_dev(W0), f32_dev(b0)
+    hp = dict(lr=case.lr, momentum=case.momentum, weight_decay=weight_decay)
+    par = SgdmParity(W0, b0, hp, rows=rows)
+    for t in range(1, steps + 1):
+        log(f"[{case.name}] sgdm step {t} tile {tile}")
+        Xb, dYb = synth.dense_inputs(case, t)
+        W_prev = host(W, rows)
+        wg.forge_wgrad_sgdm(bf16_dev(Xb), bf16_dev(dYb), W, b, tile=tile, **hp)
+        torch_mod().cuda.synchronize()
+        if rows is None:
+            g_ref, tau = oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb)
+        else:
+            g_ref, tau = oracle.wgrad_rows(Xb, dYb, rows), oracle.acc_floor_rows(Xb, dYb, rows)
+        rep = par.step(g_ref, tau, W_prev, host(W, rows), host(b, rows))
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+    return W, b

@@ -9,9 +9,9 @@ import pytest
 
 import oracle
 import synth
-from synth import DenseCase, GroupedCase
-from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
-                        log, sample_rows, torch_mod)
+from synth import DenseCase
+from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, log,
+                        run_dense_adamw, run_dense_sgdm, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,32 +30,10 @@ def _sync():
     torch_mod().cuda.synchronize()
 
 
-def run_dense_adamw(wg, case, steps, tile=0, rows=None):
-    """AdamW steps of `case` on the GPU, judged against the oracle each step."""
-    W0, m0, v0 = synth.dense_state(case)
-    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
-    par = AdamWParity(W0, m0, v0, adamw_hp(case), rows=rows)
-    for t in range(1, steps + 1):
-        log(f"[{case.name}] adamw step {t} tile {tile}")
-        Xb, dYb = synth.dense_inputs(case, t)
-        W_prev = host(W, rows)
-        wg.forge_wgrad_adamw(bf16_dev(Xb), bf16_dev(dYb), W, m, v, step=t, tile=tile,
-                             **adamw_hp(case))
-        _sync()
-        if rows is None:
-            g_ref, tau = oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb)
-        else:
-            g_ref, tau = oracle.wgrad_rows(Xb, dYb, rows), oracle.acc_floor_rows(Xb, dYb, rows)
-        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
-        log(f"  {rep}")
-        assert rep.passed, f"step {t}: {rep}"
-    return W, m, v
-
-
 RAGGED = DenseCase("ragged_77x264x200", T=77, d_in=264, d_out=200, seed_base=50000, steps=3)
 
 
-@pytest.mark.parametrize("tile", [1, 2])
+@pytest.mark.parametrize("tile", [1, 2, 3])
 def test_ragged_dense_adamw(wg, tile):
     run_dense_adamw(wg, RAGGED, RAGGED.steps, tile=tile)
 
@@ -85,7 +63,7 @@ def test_bitwise_tilings_unfused_and_repeat(wg):
     case = DenseCase("bitwise_300x520x392", T=300, d_in=520, d_out=392, seed_base=52000)
     hp = adamw_hp(case)
     results = []
-    for route in ("tile1", "tile2", "unfused", "tile1_again"):
+    for route in ("tile1", "tile2", "tile3", "unfused", "tile1_again"):
         W, m, v = _state(case)
         for t in (1, 2):
             Xb, dYb = synth.dense_inputs(case, t)
@@ -95,8 +73,8 @@ def test_bitwise_tilings_unfused_and_repeat(wg):
                 wg.forge_wgrad(X, dY, g, tile=1)
                 wg.forge_adamw(g, W, m, v, step=t, **hp)
             else:
-                wg.forge_wgrad_adamw(X, dY, W, m, v, step=t, tile=2 if route == "tile2" else 1,
-                                     **hp)
+                tile = {"tile2": 2, "tile3": 3}.get(route, 1)
+                wg.forge_wgrad_adamw(X, dY, W, m, v, step=t, tile=tile, **hp)
         _sync()
         results.append((route, host(W), host(m), host(v)))
     base = results[0]
@@ -108,7 +86,7 @@ def test_unfused_gradient_against_oracle(wg):
     torch = torch_mod()
     case = DenseCase("grad_300x520x392", T=300, d_in=520, d_out=392, seed_base=53000)
     Xb, dYb = synth.dense_inputs(case, 1)
-    for tile in (1, 2):
+    for tile in (1, 2, 3):
         g = torch.full((case.d_out, case.d_in), float("nan"), device="cuda")
         wg.forge_wgrad(bf16_dev(Xb), bf16_dev(dYb), g, tile=tile)
         _sync()
@@ -143,28 +121,6 @@ def test_clip_request_fails_closed(wg):
     assert ei.value.status == 6
     _sync()
     assert bits_equal(host(W), W_before) and not host(m).any()
-
-
-def run_dense_sgdm(wg, case, steps, tile=0, rows=None, weight_decay=0.0):
-    W0, _, _ = synth.dense_state(case)
-    b0 = np.zeros_like(W0)
-    W, b = f32_dev(W0), f32_dev(b0)
-    hp = dict(lr=case.lr, momentum=case.momentum, weight_decay=weight_decay)
-    par = SgdmParity(W0, b0, hp, rows=rows)
-    for t in range(1, steps + 1):
-        log(f"[{case.name}] sgdm step {t} tile {tile}")
-        Xb, dYb = synth.dense_inputs(case, t)
-        W_prev = host(W, rows)
-        wg.forge_wgrad_sgdm(bf16_dev(Xb), bf16_dev(dYb), W, b, tile=tile, **hp)
-        _sync()
-        if rows is None:
-            g_ref, tau = oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb)
-        else:
-            g_ref, tau = oracle.wgrad_rows(Xb, dYb, rows), oracle.acc_floor_rows(Xb, dYb, rows)
-        rep = par.step(g_ref, tau, W_prev, host(W, rows), host(b, rows))
-        log(f"  {rep}")
-        assert rep.passed, f"step {t}: {rep}"
-    return W, b
 
 
 @pytest.mark.parametrize("tile,wd", [(1, 0.0), (2, 0.01)])
@@ -234,7 +190,7 @@ def test_grouped_expert_equals_dense_call(wg):
     W0 = synth.normal_f32(80, (E, d_out, d_in), 0.02)
     Xb = synth.normal_bf16(81, (offsets[-1], d_in))
     dYb = synth.normal_bf16(82, (offsets[-1], d_out))
-    for tile in (1, 2):
+    for tile in (1, 2, 3):
         W, m, v = f32_dev(W0), f32_dev(np.zeros_like(W0)), f32_dev(np.zeros_like(W0))
         run_grouped(wg, Xb, dYb, offsets, W, m, v, 1, hp, tile=tile)
         _sync()

@@ -9,6 +9,7 @@ if the library is missing, importing the entry points raises.
 from ._lib import (  # noqa: F401
     FORGE_TILE_128x128,
     FORGE_TILE_256x128,
+    FORGE_TILE_256x256,
     FORGE_TILE_DEFAULT,
     ForgeError,
     STATUS,

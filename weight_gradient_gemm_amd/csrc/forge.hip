@@ -2,6 +2,7 @@
 // kernel launch on the caller's stream. Nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -67,6 +68,7 @@ struct TileShape {
 TileShape shape_of(forge_tile t) {
   switch (t) {
     case FORGE_TILE_128x128: return {128, 128};
+    case FORGE_TILE_256x256: return {256, 256};
     case FORGE_TILE_256x128:
     default: return {256, 128};
   }
@@ -88,34 +90,41 @@ forge_status launch_status() {
   return hipGetLastError() == hipSuccess ? FORGE_OK : FORGE_ERR_LAUNCH;
 }
 
-template <int BM, int BN, int EPI>
-forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
-  a.tiles_m = int32_t((a.d_in + BM - 1) / BM);
-  a.tiles_n = int32_t((a.d_out + BN - 1) / BN);
-  a.num_tiles = a.tiles_m * a.tiles_n;
+// Tile configurations behind the public tile ids.
+using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1>;
+using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 1>;
+using Cfg128x128 = TileCfg<128, 128, 2, 2, 32, 2>;
+
+template <class C>
+void set_grid(WgradArgs& a, int64_t experts) {
+  a.tiles_m = int32_t((a.d_in + C::BM - 1) / C::BM);
+  a.tiles_n = int32_t((a.d_out + C::BN - 1) / C::BN);
+  a.num_tiles = int32_t(a.tiles_m * a.tiles_n * experts);
   a.group_m = 4;
-  hipLaunchKernelGGL((wgrad_dense_kernel<BM, BN, 2, EPI>), dim3(a.num_tiles), dim3(kThreads), 0,
-                     s, a);
+}
+
+template <class C, int EPI>
+forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
+  set_grid<C>(a, 1);
+  hipLaunchKernelGGL((wgrad_dense_kernel<C, EPI>), dim3(a.num_tiles), dim3(C::THREADS), 0, s, a);
   return launch_status();
 }
 
 template <int EPI>
 forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
   switch (tile) {
-    case FORGE_TILE_128x128: return launch_dense_t<128, 128, EPI>(a, s);
-    case FORGE_TILE_256x128: return launch_dense_t<256, 128, EPI>(a, s);
+    case FORGE_TILE_128x128: return launch_dense_t<Cfg128x128, EPI>(a, s);
+    case FORGE_TILE_256x128: return launch_dense_t<Cfg256x128, EPI>(a, s);
+    case FORGE_TILE_256x256: return launch_dense_t<Cfg256x256, EPI>(a, s);
     default: return FORGE_ERR_TILE;
   }
 }
 
-template <int BM, int BN>
+template <class C>
 forge_status launch_grouped_t(WgradArgs a, const GroupTable& gt, int32_t E, hipStream_t s) {
-  a.tiles_m = int32_t((a.d_in + BM - 1) / BM);
-  a.tiles_n = int32_t((a.d_out + BN - 1) / BN);
-  a.num_tiles = a.tiles_m * a.tiles_n * E;
-  a.group_m = 4;
-  hipLaunchKernelGGL((wgrad_grouped_kernel<BM, BN, 2, EPI_ADAMW>), dim3(a.num_tiles),
-                     dim3(kThreads), 0, s, a, gt);
+  set_grid<C>(a, E);
+  hipLaunchKernelGGL((wgrad_grouped_kernel<C, EPI_ADAMW>), dim3(a.num_tiles), dim3(C::THREADS),
+                     0, s, a, gt);
   return launch_status();
 }
 
@@ -230,12 +239,19 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
   GroupTable gt;
   std::memset(&gt, 0, sizeof(gt));
   for (int32_t e = 0; e <= E; ++e) gt.off[e] = offsets[e];
+  // Launch order: most rows first, so the heavy experts start early and the
+  // empty ones (epilogue only) fill the tail.
+  for (int32_t e = 0; e < E; ++e) gt.order[e] = e;
+  std::stable_sort(gt.order, gt.order + E, [&](int32_t x, int32_t y) {
+    return offsets[x + 1] - offsets[x] > offsets[y + 1] - offsets[y];
+  });
   WgradArgs a = base_args(X_perm, dY_perm, W, m, v, 0, d_in, d_out);
   a.adam = make_adamw(*p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (tile) {
-    case FORGE_TILE_128x128: return launch_grouped_t<128, 128>(a, gt, E, s);
-    case FORGE_TILE_256x128: return launch_grouped_t<256, 128>(a, gt, E, s);
+    case FORGE_TILE_128x128: return launch_grouped_t<Cfg128x128>(a, gt, E, s);
+    case FORGE_TILE_256x128: return launch_grouped_t<Cfg256x128>(a, gt, E, s);
+    case FORGE_TILE_256x256: return launch_grouped_t<Cfg256x256>(a, gt, E, s);
     default: return FORGE_ERR_TILE;
   }
 }

@@ -48,9 +48,9 @@ forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
                                     const float* m, const float* v, int64_t d_in, int64_t d_out,
                                     const forge_adamw_params* p, forge_tile tile);
 
-// Largest d_in, d_out and token count the kernels index (32-bit row/column
-// indices, 64-bit element offsets).
-constexpr int64_t kMaxDim = int64_t(1) << 30;
+// Largest d_in and d_out: one LDS stage of token rows must stay within a
+// 31-bit byte window (32-bit row/column indices, 64-bit element offsets).
+constexpr int64_t kMaxDim = int64_t(1) << 22;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
 // One buffer of the optimizer state, in elements (64-bit offsets; bounded so
 // byte counts never overflow).

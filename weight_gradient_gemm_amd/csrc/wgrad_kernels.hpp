@@ -42,9 +42,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 enum Epi : int { EPI_ADAMW = 0, EPI_SGDM = 1, EPI_GRAD = 2 };
 
-constexpr int kBK = 32;          // tokens per LDS stage (same for every tile shape)
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 
 struct WgradArgs {
   const uint16_t* X;   // [rows, d_in] bf16 bits
@@ -65,6 +62,7 @@ struct WgradArgs {
 
 struct GroupTable {
   int64_t off[FORGE_MAX_EXPERTS + 1];
+  int32_t order[FORGE_MAX_EXPERTS];   // experts in launch order
 };
 
 // Row stride (elements) of an LDS stage holding `w` features per token: padded
@@ -141,72 +139,170 @@ __device__ __forceinline__ bf16x8_t load_operand(const uint16_t* s, int k0, int 
   return r;
 }
 
-template <int BM, int BN, int WAVES_M, int EPI>
+// Compile-time shape of one workgroup's tile and its LDS stage.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int OCC_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_;            // tile extent along d_in, d_out
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int BK = BK_;                      // tokens per LDS stage
+  static constexpr int OCC = OCC_;                    // workgroups per CU the registers allow
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA blocks per wave
+  static constexpr int LDX = lds_stride(BM), LDY = lds_stride(BN);
+  static constexpr int STAGE = BK * (LDX + LDY);      // elements of one LDS stage
+  static constexpr int XPT = BK * BM / 8 / THREADS;   // 16-byte global chunks per thread
+  static constexpr int YPT = BK * BN / 8 / THREADS;
+  static constexpr int STAGES = 3;                    // LDS ring depth
+  static constexpr int LDS_ELEMS = STAGES * STAGE;
+  static constexpr int NFRAG = TM + TN;               // MFMA operands per wave per chunk
+  static_assert(BK % 16 == 0, "stage must hold whole MFMA token chunks");
+  static_assert(XPT * THREADS * 8 == BK * BM && YPT * THREADS * 8 == BK * BN,
+                "stage not evenly split over threads");
+  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA block");
+};
+
+// Byte offset that lies beyond every buffer window: the hardware returns zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Raw buffer window over `bytes` bytes from `base` (reads at or past the end
+// return 0). Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > int64_t(kOOB) ? int64_t(kOOB) : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Row-major epilogue through LDS (see wgrad_tile). Each wave owns a region of
+// 32 rows x (WM + 4) floats; the 4-float pad keeps both the column-major dump
+// (16 rows per 256 bytes of banks) and the row-major read conflict-free.
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::TM][C::TN],
+                                         float* __restrict__ W, float* __restrict__ S1,
+                                         float* __restrict__ S2, int i0, int o0, int wm, int wn,
+                                         int lane, int wave, uint16_t* smem) {
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM;
+  constexpr int LD = WM + 4;                 // floats per LDS row
+  constexpr int LPR = WM / 4;                // lanes per row (float4 each)
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+  constexpr int NI = 32 / RPI;               // instructions per 32-column block
+  constexpr int BATCH = NI < 8 ? NI : 8;
+  static_assert(C::WAVES * 32 * LD * 4 <= C::LDS_ELEMS * 2, "epilogue staging exceeds LDS");
+  const int d_in = a.d_in, d_out = a.d_out;
+  __syncthreads();                           // every wave is done with the operand ring
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LD;
+  const int r_lane = lane / LPR, c_lane = (lane % LPR) * 4;
+  const int i = i0 + wm * WM + c_lane;
+  const bool i_ok = i < d_in;
+#pragma unroll
+  for (int n = 0; n < TN; ++n) {
+    // Column-major dump: lane (o = lane % 32) writes rows 4 (lane / 32) + 8 q .. + 3.
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t g = {acc[m][n][4 * q + 0], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2],
+                           acc[m][n][4 * q + 3]};
+        *reinterpret_cast<f32x4_t*>(ep + (lane & 31) * LD + m * 32 + 8 * q + 4 * (lane >> 5)) = g;
+      }
+    // LDS operations of one wave complete in order: the reads below see the dump.
+    const int o_base = o0 + wn * C::WN + n * 32;
+#pragma unroll
+    for (int j0 = 0; j0 < NI; j0 += BATCH) {
+      f32x4_t g[BATCH], w[BATCH], s1[BATCH], s2[BATCH];
+      int64_t off[BATCH];
+      bool ok[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int row = (j0 + j) * RPI + r_lane;
+        const int o = o_base + row;
+        g[j] = *reinterpret_cast<const f32x4_t*>(ep + row * LD + c_lane);
+        ok[j] = i_ok && o < d_out;
+        off[j] = int64_t(o) * d_in + i;
+        if (EPI != EPI_GRAD && ok[j]) {
+          w[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + off[j]));
+          s1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S1 + off[j]));
+          if (EPI == EPI_ADAMW)
+            s2[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S2 + off[j]));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (!ok[j]) continue;
+        f32x4_t* pw = reinterpret_cast<f32x4_t*>(W + off[j]);
+        if constexpr (EPI == EPI_GRAD) {
+          __builtin_nontemporal_store(g[j], pw);
+        } else if constexpr (EPI == EPI_ADAMW) {
+          adamw_vec4(g[j], w[j], s1[j], s2[j], a.adam);
+          __builtin_nontemporal_store(w[j], pw);
+          __builtin_nontemporal_store(s1[j], reinterpret_cast<f32x4_t*>(S1 + off[j]));
+          __builtin_nontemporal_store(s2[j], reinterpret_cast<f32x4_t*>(S2 + off[j]));
+        } else {
+          sgdm_vec4(g[j], w[j], s1[j], a.sgd);
+          __builtin_nontemporal_store(w[j], pw);
+          __builtin_nontemporal_store(s1[j], reinterpret_cast<f32x4_t*>(S1 + off[j]));
+        }
+      }
+    }
+  }
+}
+
+template <class C, int EPI>
 __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* __restrict__ X,
                                            const uint16_t* __restrict__ dY,
                                            float* __restrict__ W, float* __restrict__ S1,
                                            float* __restrict__ S2, int64_t T, int tile_m,
                                            int tile_n, uint16_t* smem) {
-  constexpr int WAVES_N = kWaves / WAVES_M;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LDX = lds_stride(BM), LDY = lds_stride(BN);
-  constexpr int STAGE = kBK * (LDX + LDY);
-  constexpr int XCH = kBK * BM / 8, YCH = kBK * BN / 8;  // 16-byte chunks per stage
-  constexpr int XPT = XCH / kThreads, YPT = YCH / kThreads;
-  static_assert(XCH % kThreads == 0 && YCH % kThreads == 0, "stage not evenly split");
-  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA block");
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
+  constexpr int LDX = C::LDX, LDY = C::LDY, STAGE = C::STAGE, XPT = C::XPT, YPT = C::YPT;
+  constexpr int NT = C::THREADS;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int d_in = a.d_in, d_out = a.d_out;
   const int i0 = tile_m * BM, o0 = tile_n * BN;
 
-  // Per-thread global chunks: chunk c = tid + kThreads * q covers row
-  // c / (W/8) of the stage and features (c % (W/8)) * 8 .. + 7.
-  int x_row[XPT], x_col[XPT], y_row[YPT], y_col[YPT];
-  bool x_ok[XPT], y_ok[YPT];
+  // Thread's chunks of a stage: chunk c = tid + NT q is token row c / (BM/8) of
+  // the stage, features (c % (BM/8)) * 8 .. + 7. Feature chunks past d_in read
+  // as zero (offset kOOB); token rows past T fall outside the stage window.
+  uint32_t x_off[XPT], y_off[YPT];
+  int x_lds[XPT], y_lds[YPT];
 #pragma unroll
   for (int q = 0; q < XPT; ++q) {
-    const int c = tid + kThreads * q;
-    x_row[q] = c / (BM / 8);
-    x_col[q] = (c % (BM / 8)) * 8;
-    x_ok[q] = i0 + x_col[q] < d_in;
+    const int c = tid + NT * q, r = c / (BM / 8), col = (c % (BM / 8)) * 8;
+    x_lds[q] = r * LDX + col;
+    x_off[q] = i0 + col < d_in ? uint32_t(r * d_in + col) * 2u : kOOB;
   }
 #pragma unroll
   for (int q = 0; q < YPT; ++q) {
-    const int c = tid + kThreads * q;
-    y_row[q] = c / (BN / 8);
-    y_col[q] = (c % (BN / 8)) * 8;
-    y_ok[q] = o0 + y_col[q] < d_out;
+    const int c = tid + NT * q, r = c / (BN / 8), col = (c % (BN / 8)) * 8;
+    y_lds[q] = r * LDY + col;
+    y_off[q] = o0 + col < d_out ? uint32_t(r * d_out + col) * 2u : kOOB;
   }
 
-  u32x4_t xr[XPT], yr[YPT];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int q = 0; q < XPT; ++q) {
-      const int64_t k = k0 + x_row[q];
-      xr[q] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (x_ok[q] && k < T)
-        xr[q] = *reinterpret_cast<const u32x4_t*>(X + k * d_in + i0 + x_col[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < YPT; ++q) {
-      const int64_t k = k0 + y_row[q];
-      yr[q] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (y_ok[q] && k < T)
-        yr[q] = *reinterpret_cast<const u32x4_t*>(dY + k * d_out + o0 + y_col[q]);
-    }
+  struct Regs {
+    u32x4_t x[XPT], y[YPT];
   };
-  auto sstore = [&](int buf) {
+  auto gload = [&](Regs& R, int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rx = window(X + k0 * d_in + i0, ((T - k0) * d_in - i0) * 2);
+    const __amdgpu_buffer_rsrc_t ry = window(dY + k0 * d_out + o0, ((T - k0) * d_out - o0) * 2);
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) R.x[q] = load16(rx, x_off[q]);
+#pragma unroll
+    for (int q = 0; q < YPT; ++q) R.y[q] = load16(ry, y_off[q]);
+  };
+  auto sstore = [&](const Regs& R, int buf) {
     uint16_t* sx = smem + buf * STAGE;
-    uint16_t* sy = sx + kBK * LDX;
+    uint16_t* sy = sx + BK * LDX;
 #pragma unroll
-    for (int q = 0; q < XPT; ++q)
-      *reinterpret_cast<u32x4_t*>(sx + x_row[q] * LDX + x_col[q]) = xr[q];
+    for (int q = 0; q < XPT; ++q) *reinterpret_cast<u32x4_t*>(sx + x_lds[q]) = R.x[q];
 #pragma unroll
-    for (int q = 0; q < YPT; ++q)
-      *reinterpret_cast<u32x4_t*>(sy + y_row[q] * LDY + y_col[q]) = yr[q];
+    for (int q = 0; q < YPT; ++q) *reinterpret_cast<u32x4_t*>(sy + y_lds[q]) = R.y[q];
   };
 
   f32x16_t acc[TM][TN];
@@ -217,95 +313,133 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
 
-  auto compute = [&](int buf) {
+  // Operand registers: two sets, alternating between consecutive 16-token
+  // chunks. Set f holds TM operands of X^T then TN operands of dY.
+  bf16x8_t frag[2][C::NFRAG];
+  auto read_frags = [&](int f, int buf, int kk) {
     const uint16_t* sx = smem + buf * STAGE;
-    const uint16_t* sy = sx + kBK * LDX;
+    const uint16_t* sy = sx + BK * LDX;
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8_t af[TM], bfrag[TN];
+    for (int m = 0; m < TM; ++m) frag[f][m] = load_operand<LDX>(sx, kk, wm * C::WM + m * 32, lane);
 #pragma unroll
-      for (int m = 0; m < TM; ++m) af[m] = load_operand<LDX>(sx, kk, wm * WM + m * 32, lane);
+    for (int n = 0; n < TN; ++n)
+      frag[f][TM + n] = load_operand<LDY>(sy, kk, wn * C::WN + n * 32, lane);
+  };
+  auto mfmas = [&](int f) {
 #pragma unroll
-      for (int n = 0; n < TN; ++n) bfrag[n] = load_operand<LDY>(sy, kk, wn * WN + n * 32, lane);
+    for (int m = 0; m < TM; ++m)
 #pragma unroll
-      for (int m = 0; m < TM; ++m)
+      for (int n = 0; n < TN; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[f][m], frag[f][TM + n],
+                                                            acc[m][n], 0, 0, 0);
+  };
+  // Interleave one MFMA with the other instruction groups of a chunk so the
+  // matrix core never waits on an issue slot: `reads` LDS reads, `loads`
+  // global loads and `writes` LDS writes spread over the chunk's MFMAs.
+  auto interleave = [&](int reads, int loads, int writes) {
 #pragma unroll
-        for (int n = 0; n < TN; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfrag[n], acc[m][n], 0, 0, 0);
+    for (int i = 0; i < TM * TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+      if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+      if (i < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+      if (i >= TM * TN - writes) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
     }
   };
 
-  const int64_t nk = (T + kBK - 1) / kBK;
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = int(kt & 1);
-      const bool more = kt + 1 < nk;
-      if (more) gload((kt + 1) * kBK);
-      compute(cur);
-      if (more) sstore(cur ^ 1);
-      __syncthreads();
-    }
-  }
-
-  // Epilogue: lane owns rows i = .. + 8q + 4 (lane / 32) + 0..3 of column o.
-  const int o_lane = lane & 31, i_lane = 4 * (lane >> 5);
+  // Mainloop over stages of BK tokens: an LDS ring of 3 stages and 3 register
+  // sets of global prefetch. At the top of stage s, LDS[s % 3] and
+  // LDS[(s+1) % 3] hold stages s and s+1 (published by earlier barriers),
+  // frag[0] holds stage s's first chunk, and the register sets hold stages
+  // s+2 and s+3 (in flight). During stage s:
+  //   - stage s+4 is requested into the set that held stage s+1;
+  //   - the chunks' operands are read one chunk ahead from LDS (the last
+  //     chunk reads stage s+1's first chunk);
+  //   - stage s+2 is written to LDS[(s+2) % 3], the buffer of stage s-1,
+  //     which every wave finished before the previous barrier.
+  // So each global load has about three stages of MFMA work to land. One
+  // barrier per stage publishes the write. Stages past the end are fetched
+  // through an empty window (zeros) into buffers nobody reads again, which
+  // keeps each stage one straight-line scheduling region.
+  constexpr int KK = BK / 16;
+  constexpr int NREAD = 2 * C::NFRAG;   // LDS transpose reads per chunk
+  constexpr int NLOAD = XPT + YPT;      // global loads (and LDS writes) per stage
+  static_assert(KK % 2 == 0, "the operand-set alternation assumes an even chunk count");
+  const int64_t nk = (T + BK - 1) / BK;
+  auto stage = [&](int64_t kt, Regs& r_load, const Regs& r_store, int buf, int buf1, int buf2) {
+    gload(r_load, (kt + 4) * BK);
 #pragma unroll
-  for (int n = 0; n < TN; ++n) {
-    const int o = o0 + wn * WN + n * 32 + o_lane;
-    if (o >= d_out) continue;
-#pragma unroll
-    for (int m = 0; m < TM; ++m) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = i0 + wm * WM + m * 32 + 8 * q + i_lane;
-        if (i >= d_in) continue;
-        const int64_t off = int64_t(o) * d_in + i;
-        const f32x4_t g = {acc[m][n][4 * q + 0], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2],
-                           acc[m][n][4 * q + 3]};
-        if constexpr (EPI == EPI_GRAD) {
-          *reinterpret_cast<f32x4_t*>(W + off) = g;
-        } else if constexpr (EPI == EPI_ADAMW) {
-          f32x4_t w = *reinterpret_cast<const f32x4_t*>(W + off);
-          f32x4_t mm = *reinterpret_cast<const f32x4_t*>(S1 + off);
-          f32x4_t vv = *reinterpret_cast<const f32x4_t*>(S2 + off);
-          adamw_vec4(g, w, mm, vv, a.adam);
-          *reinterpret_cast<f32x4_t*>(W + off) = w;
-          *reinterpret_cast<f32x4_t*>(S1 + off) = mm;
-          *reinterpret_cast<f32x4_t*>(S2 + off) = vv;
-        } else {
-          f32x4_t w = *reinterpret_cast<const f32x4_t*>(W + off);
-          f32x4_t b = *reinterpret_cast<const f32x4_t*>(S1 + off);
-          sgdm_vec4(g, w, b, a.sgd);
-          *reinterpret_cast<f32x4_t*>(W + off) = w;
-          *reinterpret_cast<f32x4_t*>(S1 + off) = b;
-        }
+    for (int kk = 0; kk < KK; ++kk) {
+      const int f = kk & 1;
+      if (kk < KK - 1) {
+        read_frags(f ^ 1, buf, (kk + 1) * 16);
+      } else {
+        read_frags(f ^ 1, buf1, 0);
       }
+      mfmas(f);
+      if (kk == KK - 1) sstore(r_store, buf2);
+      interleave(NREAD, kk == 0 ? NLOAD : 0, kk == KK - 1 ? NLOAD : 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+  if (nk > 0) {
+    Regs r0, r1, r2;
+    gload(r0, 0);
+    gload(r1, BK);
+    gload(r2, 2 * BK);
+    sstore(r0, 0);
+    sstore(r1, 1);
+    __syncthreads();
+    gload(r0, 3 * BK);
+    read_frags(0, 0, 0);
+    // Whole rounds of 3 stages keep one loop exit (so the accumulators keep
+    // their registers). Up to two extra stages read zeros: a chunk of zero
+    // products adds exactly +0 to an accumulator that is never -0 (it starts
+    // at +0 and an exact-zero sum rounds to +0), so they change no bit.
+    const int64_t rounds = (nk + 2) / 3;
+    for (int64_t r = 0; r < rounds; ++r) {
+      const int64_t kt = 3 * r;
+      stage(kt, r1, r2, 0, 1, 2);
+      stage(kt + 1, r2, r0, 1, 2, 0);
+      stage(kt + 2, r0, r1, 2, 0, 1);
     }
   }
+
+  // Epilogue. The MFMA result gives each lane 4-row pieces of one column, so a
+  // direct store touches 32 rows of W per instruction. Instead, each wave
+  // passes its accumulators through LDS one 32-column block at a time and
+  // reads them back row-major: every global instruction then covers
+  // 256 / WM whole rows of WM contiguous floats of W (and of m, v). Loads of
+  // EPI_BATCH instructions are in flight before any optimizer math.
+  epilogue<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, wave, smem);
 }
 
-template <int BM, int BN, int WAVES_M, int EPI>
-__global__ __launch_bounds__(kThreads) void wgrad_dense_kernel(WgradArgs a) {
-  constexpr int STAGE = kBK * (lds_stride(BM) + lds_stride(BN));
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+template <class C, int EPI>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
+void wgrad_dense_kernel(WgradArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   int e, tm, tn;
   map_tile(blockIdx.x, a.num_tiles, a.tiles_m, a.tiles_n, a.group_m, e, tm, tn);
-  wgrad_tile<BM, BN, WAVES_M, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, smem);
+  wgrad_tile<C, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, smem);
 }
 
-template <int BM, int BN, int WAVES_M, int EPI>
-__global__ __launch_bounds__(kThreads) void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
-  constexpr int STAGE = kBK * (lds_stride(BM) + lds_stride(BN));
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  int e, tm, tn;
-  map_tile(blockIdx.x, a.num_tiles, a.tiles_m, a.tiles_n, a.group_m, e, tm, tn);
+// Routed experts: the grid is laid out expert-major in the order of
+// GroupTable::order (largest experts first); within an expert the usual tile
+// walk applies. An expert with no rows still runs its epilogue (zero gradient).
+template <class C, int EPI>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
+void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  const int per_expert = a.tiles_m * a.tiles_n;
+  const int slot = blockIdx.x / per_expert;
+  const int e = gt.order[slot];
+  int unused, tm, tn;
+  map_tile(blockIdx.x - slot * per_expert, per_expert, a.tiles_m, a.tiles_n, a.group_m, unused,
+           tm, tn);
   const int64_t r0 = gt.off[e], r1 = gt.off[e + 1];
   const int64_t state = int64_t(e) * a.d_out * a.d_in;
-  wgrad_tile<BM, BN, WAVES_M, EPI>(a, a.X + r0 * a.d_in, a.dY + r0 * a.d_out, a.W + state,
-                                   a.S1 + state, a.S2 + state, r1 - r0, tm, tn, smem);
+  wgrad_tile<C, EPI>(a, a.X + r0 * a.d_in, a.dY + r0 * a.d_out, a.W + state, a.S1 + state,
+                     a.S2 + state, r1 - r0, tm, tn, smem);
 }
 
 // Unfused elementwise optimizers (the HBM-materialising comparison path).
