@@ -70,8 +70,8 @@ def read_traffic(workload: str, sha: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mlp_down", choices=sorted(WORKLOADS))
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--pool", type=int, default=2, help="distinct input batches cycled")

@@ -38,7 +38,11 @@ def acc_floor_rows(X_bits: np.ndarray, dY_bits: np.ndarray, rows) -> np.ndarray:
 
 
 class StateFloor:
-    """Propagated floors for the optimizer state of one tensor (or a sample)."""
+    """Propagated floors for the optimizer state of one tensor (or a sample).
+
+    Also keeps each element's gradient and floor history (float32), from which
+    the AdamW judgment forms the first-order sensitivity of the update to
+    every past gradient."""
 
     def __init__(self, shape, kind: str = "adamw", beta1: float = 0.9, beta2: float = 0.999,
                  momentum: float = 0.9):
@@ -46,9 +50,13 @@ class StateFloor:
         self.beta1, self.beta2, self.momentum = beta1, beta2, momentum
         self.m_err = np.zeros(shape, dtype=np.float64)
         self.v_err = np.zeros(shape, dtype=np.float64)
+        self.g_hist: list = []
+        self.tau_hist: list = []
 
     def update(self, tau: np.ndarray, g_ref: np.ndarray) -> None:
         tau = np.asarray(tau, dtype=np.float64)
+        self.g_hist.append(np.asarray(g_ref, dtype=np.float32))
+        self.tau_hist.append(tau.astype(np.float32))
         if self.kind == "adamw":
             g = np.abs(np.asarray(g_ref, dtype=np.float64))
             self.m_err = self.beta1 * self.m_err + (1.0 - self.beta1) * tau

@@ -62,6 +62,7 @@ class AdamWParity:
     def __init__(self, W0, m0, v0, hp, rows=None, lead=None):
         self.hp = dict(hp)
         self.rows = rows
+        self.zero_start = not (np.any(m0) or np.any(v0))
         sel = (lambda a: a) if rows is None else (lambda a: a[..., rows, :])
         self.Wr, self.mr, self.vr = sel(W0).copy(), sel(m0).copy(), sel(v0).copy()
         self.floor = oracle.StateFloor(self.Wr.shape, "adamw", hp["beta1"], hp["beta2"])
@@ -70,7 +71,7 @@ class AdamWParity:
         self.floor.update(tau, g_ref)
         Wr_new, mr, vr = oracle.adamw_step(self.Wr, self.mr, self.vr, g_ref, t, **self.hp)
         rep = judge.judge_adamw(t, W_prev_gpu, W_gpu, m_gpu, v_gpu, self.Wr, Wr_new, mr, vr,
-                                g_ref, tau, self.floor, **self.hp)
+                                g_ref, tau, self.floor, zero_start=self.zero_start, **self.hp)
         self.Wr, self.mr, self.vr = Wr_new, mr, vr
         return rep
 

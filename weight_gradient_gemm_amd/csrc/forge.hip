@@ -78,12 +78,33 @@ int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s) {
   return ((d_in + s.bm - 1) / s.bm) * ((d_out + s.bn - 1) / s.bn);
 }
 
-// Default tile: the large tile unless it leaves most compute units idle.
+// Default tile: the one with the best estimated throughput for the shape. A
+// tile's share of the matrix-core rate (measured on gfx950 for the
+// Llama-3-8B MLP-down contraction, relative to 256x256) is scaled by how well
+// its tiles fill whole waves of workgroups over the 256 compute units.
 forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts) {
   if (t != FORGE_TILE_DEFAULT) return t;
-  if (experts * count_tiles(d_in, d_out, shape_of(FORGE_TILE_256x128)) < 256)
-    return FORGE_TILE_128x128;
-  return FORGE_TILE_256x128;
+  struct Cand {
+    forge_tile id;
+    double rate;     // relative per-tile throughput
+    int64_t slots;   // concurrent workgroups on 256 CUs
+  };
+  const Cand cands[] = {{FORGE_TILE_256x256, 1.00, 256},
+                        {FORGE_TILE_256x128, 0.85, 256},
+                        {FORGE_TILE_128x128, 0.80, 512}};
+  forge_tile best = FORGE_TILE_256x128;
+  double best_score = -1.0;
+  for (const Cand& c : cands) {
+    const int64_t tiles = experts * count_tiles(d_in, d_out, shape_of(c.id));
+    const int64_t rounds = (tiles + c.slots - 1) / c.slots;
+    const double fill = double(tiles) / double(rounds * c.slots);
+    const double score = c.rate * fill;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = c.id;
+    }
+  }
+  return best;
 }
 
 forge_status launch_status() {
@@ -91,7 +112,7 @@ forge_status launch_status() {
 }
 
 // Tile configurations behind the public tile ids.
-using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1>;
+using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1, LAYOUT_T>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 1>;
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 32, 2>;
 
