@@ -45,10 +45,16 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code: comments, trailing blanks and empty
+    lines are dropped, so only a change to the code itself invalidates the
+    committed counter summaries."""
     h = hashlib.sha256()
     for fn in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "weight_gradient_gemm_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "weight_gradient_gemm_amd", "csrc", fn)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

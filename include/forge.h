@@ -91,7 +91,10 @@ enum {
  *   v_t = beta2 v_{t-1} + (1 - beta2) g^2
  *   W_t = W_{t-1} (1 - lr wd) - lr / (1 - beta1^t) * m_t / (sqrt(v_t) / sqrt(1 - beta2^t) + eps)
  * The scalars in the last line are formed on the host in double precision and
- * rounded to float32; the per-element arithmetic is float32, IEEE-rounded.
+ * rounded to float32; the per-element arithmetic is float32 with fused
+ * multiply-adds and the hardware square root and reciprocal (1 ulp each; the
+ * correctly rounded square root when eps = 0). The fused and unfused paths
+ * share that arithmetic and agree bitwise.
  * FORGE assessment, "Claim hygiene on the source": AdamW and SGD are the
  * optimizers the method covers.
  * Ranges: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0, weight_decay >= 0,
@@ -127,8 +130,15 @@ typedef struct {
 } forge_sgdm_params;
 
 /*
- * Output tile of one workgroup, named (d_in extent) x (d_out extent).
- * Every tile gives bitwise-identical results; only speed differs.
+ * Output tile of one workgroup, named (d_in extent) x (d_out extent), and how
+ * tiles are scheduled. Every choice gives bitwise-identical results (each
+ * element takes its tokens in the same order); only speed differs.
+ *   FORGE_TILE_256x128, _128x128, _256x256: one workgroup per tile.
+ *   FORGE_TILE_PERSISTENT: one workgroup per compute unit walking a list of
+ *     256x256 tiles and 256x128 half tiles; half the compute units run half a
+ *     tile out of step, which balances a fractional number of tiles per unit
+ *     and spreads the optimizer epilogues' HBM traffic over time. Dense calls
+ *     only; a grouped call treats it as FORGE_TILE_256x256.
  */
 typedef int32_t forge_tile;
 enum {
@@ -136,7 +146,8 @@ enum {
   FORGE_TILE_256x128 = 1,
   FORGE_TILE_128x128 = 2,
   FORGE_TILE_256x256 = 3,
-  FORGE_TILE_COUNT = 4
+  FORGE_TILE_PERSISTENT = 4,
+  FORGE_TILE_COUNT = 5
 };
 
 /* Maximum number of experts in one grouped call. */

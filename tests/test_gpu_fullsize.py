@@ -40,24 +40,26 @@ def test_qkv_adamw_and_sgdm(wg):
 
 
 def test_qkv_bitwise_across_tilings_full_tensors(wg):
-    """Two M x N tilings and a repeat give identical W, m, v bit patterns on
-    the whole [6144, 4096] state (FORGE assessment, P1)."""
+    """Three M x N tilings, the persistent schedule and a repeat give identical
+    W, m, v bit patterns on the whole [6144, 4096] state (FORGE assessment,
+    P1)."""
     torch = torch_mod()
     case = synth.dense_case(2)
     Xb, dYb = synth.dense_inputs(case, 1)
     X, dY = bf16_dev(Xb), bf16_dev(dYb)
     W0, m0, v0 = synth.dense_state(case)
     out = []
-    for tile in (1, 2, 1):
+    tiles = (1, 2, 3, 4, 1)
+    for tile in tiles:
         W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
         log(f"[qkv bitwise] tile {tile}")
         wg.forge_wgrad_adamw(X, dY, W, m, v, step=1, tile=tile, **adamw_hp(case))
         wg.forge_wgrad_adamw(X, dY, W, m, v, step=2, tile=tile, **adamw_hp(case))
         torch.cuda.synchronize()
         out.append(tuple(t.view(torch.int32) for t in (W, m, v)))
-    for k in (1, 2):
+    for k in range(1, len(tiles)):
         for a, b in zip(out[0], out[k]):
-            assert torch.equal(a, b), k
+            assert torch.equal(a, b), tiles[k]
 
 
 def test_lm_head_adamw_5_steps(wg):

@@ -33,9 +33,44 @@ def _sync():
 RAGGED = DenseCase("ragged_77x264x200", T=77, d_in=264, d_out=200, seed_base=50000, steps=3)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 def test_ragged_dense_adamw(wg, tile):
     run_dense_adamw(wg, RAGGED, RAGGED.steps, tile=tile)
+
+
+# 18 x 17 tiles of 256x256 (both edges ragged; the last column's second half
+# tile lies wholly past d_out): enough tiles that the persistent schedule runs
+# both phases, whole tiles and half tiles on every XCD. T = 45: one stage and
+# a 13-token tail.
+PERSIST = DenseCase("persistent_45x4360x4104", T=45, d_in=4360, d_out=4104, seed_base=55000,
+                    steps=2)
+
+
+def test_persistent_schedule_adamw(wg):
+    run_dense_adamw(wg, PERSIST, PERSIST.steps, tile=4)
+
+
+def test_persistent_gradient_bitwise_equals_grid_tiles(wg):
+    torch = torch_mod()
+    Xb, dYb = synth.dense_inputs(PERSIST, 1)
+    X, dY = bf16_dev(Xb), bf16_dev(dYb)
+    out = {}
+    for tile in (4, 3, 1):
+        g = torch.full((PERSIST.d_out, PERSIST.d_in), float("nan"), device="cuda")
+        wg.forge_wgrad(X, dY, g, tile=tile)
+        _sync()
+        out[tile] = host(g)
+    assert bits_equal(out[4], out[3]) and bits_equal(out[4], out[1])
+    rows = np.array([0, 1, 255, 256, 2047, 4095, 4096, 4103])
+    err = np.abs(out[4][rows].astype(np.float64) - oracle.wgrad_rows(Xb, dYb, rows))
+    assert np.all(err <= oracle.acc_floor_rows(Xb, dYb, rows))
+
+
+@pytest.mark.parametrize("tile", [3, 4])
+def test_eps_zero_exact_root(wg, tile):
+    case = DenseCase("eps0_77x264x200", T=77, d_in=264, d_out=200, seed_base=56000, steps=3,
+                     eps=0.0)
+    run_dense_adamw(wg, case, case.steps, tile=tile)
 
 
 def test_config0_tiny_dense_adamw(wg):
@@ -63,7 +98,7 @@ def test_bitwise_tilings_unfused_and_repeat(wg):
     case = DenseCase("bitwise_300x520x392", T=300, d_in=520, d_out=392, seed_base=52000)
     hp = adamw_hp(case)
     results = []
-    for route in ("tile1", "tile2", "tile3", "unfused", "tile1_again"):
+    for route in ("tile1", "tile2", "tile3", "tile4", "unfused", "tile1_again"):
         W, m, v = _state(case)
         for t in (1, 2):
             Xb, dYb = synth.dense_inputs(case, t)
@@ -73,7 +108,7 @@ def test_bitwise_tilings_unfused_and_repeat(wg):
                 wg.forge_wgrad(X, dY, g, tile=1)
                 wg.forge_adamw(g, W, m, v, step=t, **hp)
             else:
-                tile = {"tile2": 2, "tile3": 3}.get(route, 1)
+                tile = {"tile2": 2, "tile3": 3, "tile4": 4}.get(route, 1)
                 wg.forge_wgrad_adamw(X, dY, W, m, v, step=t, tile=tile, **hp)
         _sync()
         results.append((route, host(W), host(m), host(v)))
@@ -86,7 +121,7 @@ def test_unfused_gradient_against_oracle(wg):
     torch = torch_mod()
     case = DenseCase("grad_300x520x392", T=300, d_in=520, d_out=392, seed_base=53000)
     Xb, dYb = synth.dense_inputs(case, 1)
-    for tile in (1, 2, 3):
+    for tile in (1, 2, 3, 4):
         g = torch.full((case.d_out, case.d_in), float("nan"), device="cuda")
         wg.forge_wgrad(bf16_dev(Xb), bf16_dev(dYb), g, tile=tile)
         _sync()
@@ -123,7 +158,7 @@ def test_clip_request_fails_closed(wg):
     assert bits_equal(host(W), W_before) and not host(m).any()
 
 
-@pytest.mark.parametrize("tile,wd", [(1, 0.0), (2, 0.01)])
+@pytest.mark.parametrize("tile,wd", [(1, 0.0), (2, 0.01), (4, 0.01)])
 def test_ragged_dense_sgdm(wg, tile, wd):
     run_dense_sgdm(wg, RAGGED, 3, tile=tile, weight_decay=wd)
 

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     FORGE_TILE_128x128,
     FORGE_TILE_256x128,
     FORGE_TILE_256x256,
+    FORGE_TILE_PERSISTENT,
     FORGE_TILE_DEFAULT,
     ForgeError,
     STATUS,

@@ -17,6 +17,7 @@ FORGE_TILE_DEFAULT = 0
 FORGE_TILE_256x128 = 1
 FORGE_TILE_128x128 = 2
 FORGE_TILE_256x256 = 3
+FORGE_TILE_PERSISTENT = 4
 
 STATUS = {
     0: "FORGE_OK", 1: "FORGE_ERR_NULL", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_ALIGN",

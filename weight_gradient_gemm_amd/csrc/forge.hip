@@ -17,6 +17,8 @@ namespace {
 constexpr int kMaxDevices = 64;
 // Per-device verdict of the architecture check: 0 unknown, 1 gfx950, -1 other.
 std::atomic<int> g_arch_ok[kMaxDevices];
+// Per-device compute-unit count (0 unknown).
+std::atomic<int> g_cu_count[kMaxDevices];
 
 forge_status check_device() {
   int dev = -1;
@@ -32,9 +34,19 @@ forge_status check_device() {
       return FORGE_ERR_DEVICE;
     }
     v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_ok[dev].store(v, std::memory_order_relaxed);
   }
   return v == 1 ? FORGE_OK : FORGE_ERR_DEVICE;
+}
+
+// Workgroups of a persistent launch on the current device: one per compute
+// unit, rounded down to whole pairs per XCD (8 XCDs), or 0 if too few.
+int persistent_grid() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+  return (cus / 16) * 16;
 }
 
 AdamWConsts make_adamw(const forge_adamw_params& p) {
@@ -68,7 +80,8 @@ struct TileShape {
 TileShape shape_of(forge_tile t) {
   switch (t) {
     case FORGE_TILE_128x128: return {128, 128};
-    case FORGE_TILE_256x256: return {256, 256};
+    case FORGE_TILE_256x256:
+    case FORGE_TILE_PERSISTENT: return {256, 256};
     case FORGE_TILE_256x128:
     default: return {256, 128};
   }
@@ -82,7 +95,28 @@ int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s) {
 // tile's share of the matrix-core rate (measured on gfx950 for the
 // Llama-3-8B MLP-down contraction, relative to 256x256) is scaled by how well
 // its tiles fill whole waves of workgroups over the 256 compute units.
+// Makespan, in full-tile times, of the persistent schedule for `tiles` 256x256
+// tiles on `grid` workgroups (stagger mode 1: odd XCDs half a tile behind). A
+// half tile costs 0.6 of a full one (it runs at ~85% of the full tile's rate).
+double persistent_makespan(int64_t tiles, int grid) {
+  const int nw = grid / 8;
+  double worst = 0.0;
+  for (int xcd = 0; xcd < 8; ++xcd) {
+    const int64_t per = tiles / 8, rem = tiles % 8;
+    const int R = int(per + (xcd < rem ? 1 : 0));
+    const int phase = (xcd & 1) && R >= nw ? 1 : 0;
+    for (int j = 0; j < nw; ++j) {
+      double t = 0.0;
+      int tile, half;
+      for (int k = 0; schedule_item(k, j, nw, R, phase, tile, half); ++k) t += half < 0 ? 1.0 : 0.6;
+      worst = std::max(worst, t);
+    }
+  }
+  return worst;
+}
+
 forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts) {
+  if (experts > 1 && t == FORGE_TILE_PERSISTENT) return FORGE_TILE_256x256;
   if (t != FORGE_TILE_DEFAULT) return t;
   struct Cand {
     forge_tile id;
@@ -103,6 +137,13 @@ forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t exper
       best_score = score;
       best = c.id;
     }
+  }
+  // The persistent schedule: the 256x256 tile rate, balanced to half tiles.
+  const int grid = persistent_grid();
+  const int64_t tiles = count_tiles(d_in, d_out, shape_of(FORGE_TILE_256x256));
+  if (experts == 1 && grid > 0 && tiles >= grid) {
+    const double score = double(tiles) / (double(grid) * persistent_makespan(tiles, grid));
+    if (score > best_score + 1e-9) best = FORGE_TILE_PERSISTENT;
   }
   return best;
 }
@@ -131,23 +172,75 @@ forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
   return launch_status();
 }
 
+// Stagger mode of the persistent kernel: odd XCDs half a tile behind.
+constexpr int kStagger = 1;
+
+template <int EPI>
+forge_status launch_persistent(WgradArgs a, hipStream_t s) {
+  set_grid<Cfg256x256>(a, 1);
+  const int grid = persistent_grid();
+  if (grid <= 0) return launch_dense_t<Cfg256x256, EPI>(a, s);
+  hipLaunchKernelGGL((wgrad_persistent_kernel<Cfg256x256, Cfg256x128, EPI>), dim3(grid),
+                     dim3(Cfg256x256::THREADS), 0, s, a, kStagger);
+  return launch_status();
+}
+
 template <int EPI>
 forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
   switch (tile) {
     case FORGE_TILE_128x128: return launch_dense_t<Cfg128x128, EPI>(a, s);
     case FORGE_TILE_256x128: return launch_dense_t<Cfg256x128, EPI>(a, s);
     case FORGE_TILE_256x256: return launch_dense_t<Cfg256x256, EPI>(a, s);
+    case FORGE_TILE_PERSISTENT: return launch_persistent<EPI>(a, s);
     default: return FORGE_ERR_TILE;
   }
 }
 
-template <class C>
+// AdamW epilogue variant: the exact square root when eps = 0.
+template <template <int> class F, class... Args>
+forge_status with_adamw_epi(const forge_adamw_params& p, Args&&... args) {
+  return p.eps > 0.0 ? F<EPI_ADAMW>::run(args...) : F<EPI_ADAMW_EXACT>::run(args...);
+}
+
+template <int EPI>
+struct DenseLaunch {
+  static forge_status run(const WgradArgs& a, forge_tile tile, hipStream_t s) {
+    return launch_dense<EPI>(a, tile, s);
+  }
+};
+
+template <class C, int EPI>
 forge_status launch_grouped_t(WgradArgs a, const GroupTable& gt, int32_t E, hipStream_t s) {
   set_grid<C>(a, E);
-  hipLaunchKernelGGL((wgrad_grouped_kernel<C, EPI_ADAMW>), dim3(a.num_tiles), dim3(C::THREADS),
-                     0, s, a, gt);
+  hipLaunchKernelGGL((wgrad_grouped_kernel<C, EPI>), dim3(a.num_tiles), dim3(C::THREADS), 0, s,
+                     a, gt);
   return launch_status();
 }
+
+template <int EPI>
+struct GroupedLaunch {
+  static forge_status run(const WgradArgs& a, const GroupTable& gt, int32_t E, forge_tile tile,
+                          hipStream_t s) {
+    switch (tile) {
+      case FORGE_TILE_128x128: return launch_grouped_t<Cfg128x128, EPI>(a, gt, E, s);
+      case FORGE_TILE_256x128: return launch_grouped_t<Cfg256x128, EPI>(a, gt, E, s);
+      case FORGE_TILE_256x256: return launch_grouped_t<Cfg256x256, EPI>(a, gt, E, s);
+      default: return FORGE_ERR_TILE;
+    }
+  }
+};
+
+template <int EPI>
+struct ElementwiseAdamW {
+  static forge_status run(const float* grad, float* W, float* m, float* v, int64_t n,
+                          const AdamWConsts& c, hipStream_t s) {
+    const int64_t n4 = (n + 3) / 4;
+    const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
+    hipLaunchKernelGGL(adamw_elementwise_kernel<EPI == EPI_ADAMW_EXACT>, dim3(blocks), dim3(256),
+                       0, s, grad, W, m, v, n, c);
+    return launch_status();
+  }
+};
 
 WgradArgs base_args(const void* X, const void* dY, float* W, float* S1, float* S2, int64_t T,
                     int64_t d_in, int64_t d_out) {
@@ -182,13 +275,13 @@ FORGE_API forge_status forge_wgrad_adamw(const void* X, const void* dY, float* W
                                          void* stream) {
   if (forge_status s = validate_wgrad_adamw(X, dY, W, m, v, T, d_in, d_out, p, tile)) return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
   tile = resolve_tile(tile, d_in, d_out, 1);
   if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
-  if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
   WgradArgs a = base_args(X, dY, W, m, v, T, d_in, d_out);
   a.adam = make_adamw(*p);
-  return launch_dense<EPI_ADAMW>(a, tile, static_cast<hipStream_t>(stream));
+  return with_adamw_epi<DenseLaunch>(*p, a, tile, static_cast<hipStream_t>(stream));
 }
 
 FORGE_API forge_status forge_wgrad_sgdm(const void* X, const void* dY, float* W, float* mom,
@@ -197,9 +290,9 @@ FORGE_API forge_status forge_wgrad_sgdm(const void* X, const void* dY, float* W,
                                         void* stream) {
   if (forge_status s = validate_wgrad_sgdm(X, dY, W, mom, T, d_in, d_out, p, tile)) return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
   tile = resolve_tile(tile, d_in, d_out, 1);
   if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
-  if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
   WgradArgs a = base_args(X, dY, W, mom, nullptr, T, d_in, d_out);
   a.sgd = make_sgdm(*p);
@@ -210,9 +303,9 @@ FORGE_API forge_status forge_wgrad(const void* X, const void* dY, float* grad, i
                                    int64_t d_in, int64_t d_out, forge_tile tile, void* stream) {
   if (forge_status s = validate_wgrad(X, dY, grad, T, d_in, d_out, tile)) return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
   tile = resolve_tile(tile, d_in, d_out, 1);
   if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
-  if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
   WgradArgs a = base_args(X, dY, grad, nullptr, nullptr, T, d_in, d_out);
   return launch_dense<EPI_GRAD>(a, tile, static_cast<hipStream_t>(stream));
@@ -224,11 +317,8 @@ FORGE_API forge_status forge_adamw(const float* grad, float* W, float* m, float*
   if (n == 0) return FORGE_OK;
   if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
-  const int64_t n4 = (n + 3) / 4;
-  const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
-  hipLaunchKernelGGL(adamw_elementwise_kernel, dim3(blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), grad, W, m, v, n, make_adamw(*p));
-  return launch_status();
+  return with_adamw_epi<ElementwiseAdamW>(*p, grad, W, m, v, n, make_adamw(*p),
+                                          static_cast<hipStream_t>(stream));
 }
 
 FORGE_API forge_status forge_sgdm(const float* grad, float* W, float* mom, int64_t n,
@@ -253,9 +343,9 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
                                               p, tile))
     return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
   tile = resolve_tile(tile, d_in, d_out, E);
   if (!grid_fits(d_in, d_out, tile, E)) return FORGE_ERR_SHAPE;
-  if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
   GroupTable gt;
   std::memset(&gt, 0, sizeof(gt));
@@ -268,13 +358,7 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
   });
   WgradArgs a = base_args(X_perm, dY_perm, W, m, v, 0, d_in, d_out);
   a.adam = make_adamw(*p);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (tile) {
-    case FORGE_TILE_128x128: return launch_grouped_t<Cfg128x128>(a, gt, E, s);
-    case FORGE_TILE_256x128: return launch_grouped_t<Cfg256x128>(a, gt, E, s);
-    case FORGE_TILE_256x256: return launch_grouped_t<Cfg256x256>(a, gt, E, s);
-    default: return FORGE_ERR_TILE;
-  }
+  return with_adamw_epi<GroupedLaunch>(*p, a, gt, E, tile, static_cast<hipStream_t>(stream));
 }
 
 FORGE_API const char* forge_status_string(forge_status s) {

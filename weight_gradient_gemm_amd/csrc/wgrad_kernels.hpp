@@ -9,21 +9,22 @@
 //
 // Mainloop: bf16 MFMA v_mfma_f32_32x32x16_bf16, 4 waves per workgroup, each
 // wave owning a (BM/WAVES_M) x (BN/WAVES_N) block of the tile. Both operands
-// have the token axis strided (X and dY are row-major [T, d]), so tiles are
-// staged through LDS in their natural [token][feature] layout with coalesced
-// 16-byte loads along the feature axis, and the MFMA operands (8 consecutive
-// tokens per lane) are gathered with the gfx950 LDS transpose read
-// ds_read_b64_tr_b16. Stages of 32 tokens, double-buffered, one barrier per
-// stage.
+// have the token axis strided (X and dY are row-major [T, d]) while an MFMA
+// operand needs 8 consecutive tokens per lane, so every stage of 32 tokens is
+// transposed on its way through LDS: either in registers before the LDS store
+// (LAYOUT_T, one 16-byte LDS read per operand) or by the gfx950 LDS transpose
+// read (LAYOUT_TR). A ring of 3 LDS stages and 3 register sets of global
+// prefetch, one barrier per stage.
 //
 // Order of accumulation: for every element, the tokens enter in ascending
-// chunks of 16 through one accumulator, whatever the tile shape. Ragged token
-// tails are zero-filled, so every tile shape and the grouped variant see the
-// same chunk sequence, which makes the result bitwise partition-independent.
+// chunks of 16 through one accumulator, whatever the tile shape or schedule.
+// Ragged token tails are zero-filled, so every tile shape, the persistent
+// schedule and the grouped variant see the same chunk sequence, which makes
+// the result bitwise partition-independent.
 //
-// Epilogue: the MFMA 32x32 result layout gives each lane 4 consecutive rows
-// (d_in indices) of one column (a d_out index): exactly 16 contiguous bytes of
-// W, m, v in their [d_out, d_in] layout, so the state moves as float4.
+// Epilogue: accumulators pass through LDS to a row-major layout, then the
+// optimizer updates W and its state with whole-row 16-byte accesses,
+// software-pipelined so state loads overlap the arithmetic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,7 +41,13 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-enum Epi : int { EPI_ADAMW = 0, EPI_SGDM = 1, EPI_GRAD = 2 };
+// EPI_ADAMW_EXACT is AdamW with eps = 0, where the square root must also be
+// exact on float32 denormals.
+enum Epi : int { EPI_ADAMW = 0, EPI_SGDM = 1, EPI_GRAD = 2, EPI_ADAMW_EXACT = 3 };
+
+__host__ __device__ constexpr bool is_adamw(int epi) {
+  return epi == EPI_ADAMW || epi == EPI_ADAMW_EXACT;
+}
 
 
 struct WgradArgs {
@@ -72,6 +79,18 @@ __host__ __device__ constexpr int lds_stride(int w) {
   return w + ((((w * 2) % 256) == 0) ? 32 : (64 - (w * 2) % 256 + 256) % 256 / 2);
 }
 
+// Tile grid position of logical tile t of the grouped walk (see map_tile).
+__host__ __device__ inline void grouped_walk(int t, int tiles_m, int tiles_n, int group_m, int& tm,
+                                             int& tn) {
+  const int group_size = group_m * tiles_n;
+  const int g = t / group_size;
+  const int first_m = g * group_m;
+  const int gm = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+  const int r = t - g * group_size;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
 // Workgroup -> tile. Workgroups are dispatched round-robin over the 8 XCDs, so
 // block b runs on XCD b % 8. Remap so that each XCD gets one contiguous range
 // of logical tiles (its L2 then serves neighbouring tiles), then walk the
@@ -84,23 +103,17 @@ __device__ __forceinline__ void map_tile(int b, int num_tiles, int tiles_m, int 
                                 : rem * (per + 1) + (xcd - rem) * per + local;
   const int per_expert = tiles_m * tiles_n;
   e = logical / per_expert;
-  const int t = logical - e * per_expert;
-  const int group_size = group_m * tiles_n;
-  const int g = t / group_size;
-  const int first_m = g * group_m;
-  const int gm = min(tiles_m - first_m, group_m);
-  const int r = t - g * group_size;
-  tm = first_m + r % gm;
-  tn = r / gm;
+  grouped_walk(logical - e * per_expert, tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // The optimizer on the 4 consecutive elements one lane owns.
+template <bool EXACT_SQRT>
 __device__ __forceinline__ void adamw_vec4(const f32x4_t& g, f32x4_t& w, f32x4_t& m, f32x4_t& v,
                                            const AdamWConsts& c) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float wj = w[j], mj = m[j], vj = v[j];
-    adamw_elem(g[j], wj, mj, vj, c);
+    adamw_elem<EXACT_SQRT>(g[j], wj, mj, vj, c);
     w[j] = wj;
     m[j] = mj;
     v[j] = vj;
@@ -191,13 +204,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* base, int64
                                            0x00020000);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window32(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+#ifndef FORGE_EPI_UNIT
+#define FORGE_EPI_UNIT 4      // row instructions per epilogue unit
+#endif
+#ifndef FORGE_EPI_DEPTH
+#define FORGE_EPI_DEPTH 2     // units whose state loads are in flight together
+#endif
+#ifndef FORGE_EPI_AUX
+#define FORGE_EPI_AUX 0       // cache policy of the state loads and stores
+#endif
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                        const f32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)voff, (int)soff,
+                                         FORGE_EPI_AUX);
+}
+
+__device__ __forceinline__ f32x4_t load16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(
+      f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, FORGE_EPI_AUX));
 }
 
 // Row-major epilogue through LDS (see wgrad_tile). Each wave owns a region of
 // 32 rows x (WM + 4) floats; the 4-float pad keeps both the column-major dump
 // (16 rows per 256 bytes of banks) and the row-major read conflict-free.
+//
+// The wave's 32-column blocks are cut into units of FORGE_EPI_UNIT row
+// instructions and software-pipelined: the state loads of the next
+// FORGE_EPI_DEPTH - 1 units are issued before a unit's optimizer math and
+// stores, so memory latency overlaps the arithmetic. (On this chip family
+// the vector-memory counter covers stores as well as loads and drains in
+// issue order, so loads issued after a unit's stores would also wait for
+// those stores; issuing them first keeps the stores in flight.) State is
+// addressed through buffer windows of one 32-row block: rows past d_out lie
+// beyond the window (loads read 0, stores are dropped) and columns past d_in
+// get an out-of-window lane offset, so no lane needs a branch.
 template <class C, int EPI>
 __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::TM][C::TN],
                                          float* __restrict__ W, float* __restrict__ S1,
@@ -208,17 +258,28 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   constexpr int LPR = WM / 4;                // lanes per row (float4 each)
   constexpr int RPI = 64 / LPR;              // rows per instruction
   constexpr int NI = 32 / RPI;               // instructions per 32-column block
-  constexpr int BATCH = NI < 8 ? NI : 8;
+  constexpr int B = NI < FORGE_EPI_UNIT ? NI : FORGE_EPI_UNIT;
+  constexpr int UPB = NI / B;                // units per block
+  constexpr int U = TN * UPB;
+  constexpr int D = FORGE_EPI_DEPTH;
+  constexpr int NS = is_adamw(EPI) ? 3 : (EPI == EPI_SGDM ? 2 : 0);   // state arrays read
+  static_assert(NI % B == 0 && D >= 1, "epilogue units must tile a block");
   static_assert(C::WAVES * 32 * LD * 4 <= C::LDS_ELEMS * 2, "epilogue staging exceeds LDS");
   const int d_in = a.d_in, d_out = a.d_out;
   __syncthreads();                           // every wave is done with the operand ring
   float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LD;
   const int r_lane = lane / LPR, c_lane = (lane % LPR) * 4;
-  const int i = i0 + wm * WM + c_lane;
-  const bool i_ok = i < d_in;
-#pragma unroll
-  for (int n = 0; n < TN; ++n) {
-    // Column-major dump: lane (o = lane % 32) writes rows 4 (lane / 32) + 8 q .. + 3.
+  const int iw0 = i0 + wm * WM;
+  const uint32_t voff = iw0 + c_lane < d_in ? uint32_t(r_lane * d_in + c_lane) * 4u : kOOB;
+  const uint32_t inst_bytes = uint32_t(RPI) * uint32_t(d_in) * 4u;   // rows per instruction
+  float* const arr[3] = {W, S1, S2};
+  // Window over array k from the wave's first column of block n's first row.
+  auto block_window = [&](int k, int n) {
+    const int64_t ob = int64_t(o0) + wn * C::WN + n * 32;
+    return window(arr[k] + ob * d_in + iw0, ((int64_t(d_out) - ob) * d_in - iw0) * 4);
+  };
+  auto dump = [&](int n) {
+    // Column-major: lane (o = lane % 32) writes rows 4 (lane / 32) + 8 q .. + 3.
 #pragma unroll
     for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -227,45 +288,54 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
                            acc[m][n][4 * q + 3]};
         *reinterpret_cast<f32x4_t*>(ep + (lane & 31) * LD + m * 32 + 8 * q + 4 * (lane >> 5)) = g;
       }
-    // LDS operations of one wave complete in order: the reads below see the dump.
-    const int o_base = o0 + wn * C::WN + n * 32;
+  };
+  f32x4_t st[D][B][NS > 0 ? NS : 1];
+  auto issue = [&](int u) {
+    const int n = u / UPB, j0 = (u % UPB) * B;
 #pragma unroll
-    for (int j0 = 0; j0 < NI; j0 += BATCH) {
-      f32x4_t g[BATCH], w[BATCH], s1[BATCH], s2[BATCH];
-      int64_t off[BATCH];
-      bool ok[BATCH];
+    for (int k = 0; k < NS; ++k) {
+      const __amdgpu_buffer_rsrc_t r = block_window(k, n);
 #pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        const int row = (j0 + j) * RPI + r_lane;
-        const int o = o_base + row;
-        g[j] = *reinterpret_cast<const f32x4_t*>(ep + row * LD + c_lane);
-        ok[j] = i_ok && o < d_out;
-        off[j] = int64_t(o) * d_in + i;
-        if (EPI != EPI_GRAD && ok[j]) {
-          w[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + off[j]));
-          s1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S1 + off[j]));
-          if (EPI == EPI_ADAMW)
-            s2[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S2 + off[j]));
-        }
+      for (int j = 0; j < B; ++j) st[u % D][j][k] = load16f(r, voff, (j0 + j) * inst_bytes);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D - 1 && u < U; ++u) issue(u);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u + D - 1 < U) issue(u + D - 1);
+    const int n = u / UPB, j0 = (u % UPB) * B;
+    // LDS operations of one wave complete in order: the reads below see the
+    // dump, and the dump follows the previous block's reads.
+    if (u % UPB == 0) dump(n);
+    f32x4_t g[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      g[j] = *reinterpret_cast<const f32x4_t*>(ep + ((j0 + j) * RPI + r_lane) * LD + c_lane);
+    const __amdgpu_buffer_rsrc_t rw = block_window(0, n);
+    if constexpr (EPI == EPI_GRAD) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) store16(rw, voff, (j0 + j) * inst_bytes, g[j]);
+    } else if constexpr (is_adamw(EPI)) {
+      const __amdgpu_buffer_rsrc_t r1 = block_window(1, n), r2 = block_window(2, n);
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        f32x4_t& s = st[u % D][j][0];
+        adamw_vec4<EPI == EPI_ADAMW_EXACT>(g[j], s, st[u % D][j][1], st[u % D][j][2], a.adam);
+        store16(rw, voff, (j0 + j) * inst_bytes, s);
+        store16(r1, voff, (j0 + j) * inst_bytes, st[u % D][j][1]);
+        store16(r2, voff, (j0 + j) * inst_bytes, st[u % D][j][2]);
       }
+    } else {
+      const __amdgpu_buffer_rsrc_t r1 = block_window(1, n);
 #pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        if (!ok[j]) continue;
-        f32x4_t* pw = reinterpret_cast<f32x4_t*>(W + off[j]);
-        if constexpr (EPI == EPI_GRAD) {
-          __builtin_nontemporal_store(g[j], pw);
-        } else if constexpr (EPI == EPI_ADAMW) {
-          adamw_vec4(g[j], w[j], s1[j], s2[j], a.adam);
-          __builtin_nontemporal_store(w[j], pw);
-          __builtin_nontemporal_store(s1[j], reinterpret_cast<f32x4_t*>(S1 + off[j]));
-          __builtin_nontemporal_store(s2[j], reinterpret_cast<f32x4_t*>(S2 + off[j]));
-        } else {
-          sgdm_vec4(g[j], w[j], s1[j], a.sgd);
-          __builtin_nontemporal_store(w[j], pw);
-          __builtin_nontemporal_store(s1[j], reinterpret_cast<f32x4_t*>(S1 + off[j]));
-        }
+      for (int j = 0; j < B; ++j) {
+        sgdm_vec4(g[j], st[u % D][j][0], st[u % D][j][1], a.sgd);
+        store16(rw, voff, (j0 + j) * inst_bytes, st[u % D][j][0]);
+        store16(r1, voff, (j0 + j) * inst_bytes, st[u % D][j][1]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -279,7 +349,10 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
   constexpr int LDX = C::LDX, LDY = C::LDY, STAGE = C::STAGE, XPT = C::XPT, YPT = C::YPT;
   constexpr int NT = C::THREADS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform; readfirstlane lets the compiler keep what
+  // derives from it (buffer windows, tile offsets) in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int d_in = a.d_in, d_out = a.d_out;
   const int i0 = tile_m * BM, o0 = tile_n * BN;
@@ -308,8 +381,7 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
   // groups; b keeps the MFMA reads (features c0 + lane % 32) and the
   // transposed writes (features 8 (lane % 32) + j) free of bank conflicts
   // under those rules (and under plain 16-lane groups), checked exhaustively.
-  const bool t_is_x = C::LAYOUT == LAYOUT_T &&
-                      __builtin_amdgcn_readfirstlane(wave) < C::XBLK / 64;
+  const bool t_is_x = C::LAYOUT == LAYOUT_T && wave < C::XBLK / 64;
   const int t_blk = t_is_x ? tid : tid - C::XBLK;
   const int t_nch = t_is_x ? BM / 8 : BN / 8;
   const int t_chunk = t_blk % t_nch, t_tg = t_blk / t_nch;
@@ -340,19 +412,37 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
     }
   }
 
-  auto gload = [&](Regs& R, int64_t k0) {
+  // Stage loads walk the token axis in order with running pointers. The
+  // window of stage s covers only its own token rows (BK, the tail, or none),
+  // so rows past T read as zero; its size fits 32 bits and takes a few
+  // scalar instructions per stage.
+  const int nfull = int(T / BK), tail = int(T - int64_t(nfull) * BK);
+  int g_stage = 0;
+  const uint16_t* g_x = X + i0;                  // LAYOUT_TR
+  const uint16_t* g_y = dY + o0;
+  const int t_dim_s = __builtin_amdgcn_readfirstlane(t_dim);
+  const uint16_t* g_s = t_src + t_c0;            // LAYOUT_T
+  auto stage_bytes = [&](int dim, int c0) {
+    const int rows = g_stage < nfull ? BK : (g_stage == nfull ? tail : 0);
+    const int n = rows * dim - c0;               // c0 >= dim: a tile past the edge
+    return n > 0 ? uint32_t(n) * 2u : 0u;
+  };
+  auto gload = [&](Regs& R) {
     if constexpr (C::LAYOUT == LAYOUT_TR) {
-      const __amdgpu_buffer_rsrc_t rx = window(X + k0 * d_in + i0, ((T - k0) * d_in - i0) * 2);
-      const __amdgpu_buffer_rsrc_t ry =
-          window(dY + k0 * d_out + o0, ((T - k0) * d_out - o0) * 2);
+      const __amdgpu_buffer_rsrc_t rx = window32(g_x, stage_bytes(d_in, i0));
+      const __amdgpu_buffer_rsrc_t ry = window32(g_y, stage_bytes(d_out, o0));
+      g_x += BK * d_in;
+      g_y += BK * d_out;
+      ++g_stage;
 #pragma unroll
       for (int q = 0; q < XPT; ++q) R.r[q] = load16(rx, c_off[q]);
 #pragma unroll
       for (int q = 0; q < YPT; ++q) R.r[XPT + q] = load16(ry, c_off[XPT + q]);
     } else {
-      const int dim = __builtin_amdgcn_readfirstlane(t_dim);
-      const __amdgpu_buffer_rsrc_t rs =
-          window(t_src + k0 * dim + t_c0, ((T - k0) * dim - t_c0) * 2);
+      const int dim = t_dim_s;
+      const __amdgpu_buffer_rsrc_t rs = window32(g_s, stage_bytes(dim, t_c0));
+      g_s += BK * dim;
+      ++g_stage;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         R.r[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
@@ -448,9 +538,9 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
   constexpr int NREAD = C::LAYOUT == LAYOUT_TR ? 2 * C::NFRAG : C::NFRAG;
   constexpr int NLOAD = C::NLOAD;
   static_assert(KK % 2 == 0, "the operand-set alternation assumes an even chunk count");
-  const int64_t nk = (T + BK - 1) / BK;
-  auto stage = [&](int64_t kt, Regs& r_load, const Regs& r_store, int buf, int buf1, int buf2) {
-    gload(r_load, (kt + 4) * BK);
+  const int nk = int((T + BK - 1) / BK);
+  auto stage = [&](Regs& r_load, const Regs& r_store, int buf, int buf1, int buf2) {
+    gload(r_load);                               // stage s + 4 during stage s
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int f = kk & 1;
@@ -468,24 +558,23 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
   };
   if (nk > 0) {
     Regs r0, r1, r2;
-    gload(r0, 0);
-    gload(r1, BK);
-    gload(r2, 2 * BK);
+    gload(r0);
+    gload(r1);
+    gload(r2);
     sstore(r0, 0);
     sstore(r1, 1);
     __syncthreads();
-    gload(r0, 3 * BK);
+    gload(r0);
     read_frags(0, 0, 0);
     // Whole rounds of 3 stages keep one loop exit (so the accumulators keep
     // their registers). Up to two extra stages read zeros: a chunk of zero
     // products adds exactly +0 to an accumulator that is never -0 (it starts
     // at +0 and an exact-zero sum rounds to +0), so they change no bit.
-    const int64_t rounds = (nk + 2) / 3;
-    for (int64_t r = 0; r < rounds; ++r) {
-      const int64_t kt = 3 * r;
-      stage(kt, r1, r2, 0, 1, 2);
-      stage(kt + 1, r2, r0, 1, 2, 0);
-      stage(kt + 2, r0, r1, 2, 0, 1);
+    const int rounds = (nk + 2) / 3;
+    for (int r = 0; r < rounds; ++r) {
+      stage(r1, r2, 0, 1, 2);
+      stage(r2, r0, 1, 2, 0);
+      stage(r0, r1, 2, 0, 1);
     }
   }
 
@@ -526,7 +615,97 @@ void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
                      a.S2 + state, r1 - r0, tm, tn, smem);
 }
 
+// Persistent schedule. One workgroup per CU walks a list of items, each a full
+// tile (BM x BN) or a half tile (BM x BN/2, the column halves of a full tile).
+// The workers of a group share a contiguous range of R full tiles of the
+// grouped tile order; round k of the group covers consecutive tiles, so the
+// tiles running together share operand rows and columns in L2.
+//   phase 0: rounds of ng full tiles, then the remainder r: as 2r half tiles
+//            when 2r <= ng (the round takes half a tile's time), else as r
+//            full tiles.
+//   phase 1: the same after a first round of ng half tiles (ng/2 full tiles).
+// Groups in phase 1 run half a tile out of step with groups in phase 0, so
+// only half the chip is in the HBM-bound optimizer epilogue at any time, and
+// a remainder of half a round per worker (3.5 tiles per CU, say) is balanced
+// exactly. Returns false when worker j has no item k.
+__host__ __device__ inline bool schedule_item(int k, int j, int ng, int R, int phase, int& tile,
+                                              int& half) {
+  int pos = 0;
+  if (phase) {
+    if (k == 0) {
+      tile = j >> 1;
+      half = j & 1;
+      return true;
+    }
+    --k;
+    pos = ng >> 1;
+  }
+  const int F = R - pos, nf = F / ng, r = F - nf * ng;
+  if (k < nf) {
+    tile = pos + k * ng + j;
+    half = -1;
+    return true;
+  }
+  if (k > nf) return false;
+  pos += nf * ng;
+  if (2 * r <= ng) {
+    if (j >= 2 * r) return false;
+    tile = pos + (j >> 1);
+    half = j & 1;
+    return true;
+  }
+  if (j >= r) return false;
+  tile = pos + j;
+  half = -1;
+  return true;
+}
+
+// Persistent dense kernel over the schedule above. The grid is 8 * nw
+// workgroups (nw per XCD, even). Stagger mode 1: each XCD is a group of nw
+// workers, odd XCDs in phase 1. Mode 2: each XCD holds two groups of nw / 2
+// (even and odd workers), the odd group in phase 1. Mode 0: one group per XCD,
+// all in phase 0. Full tiles use CF, half tiles CH (same BM and threads, half
+// the BN); each element still takes its tokens in ascending 16-token chunks
+// through one accumulator, so the result is bitwise that of any other tiling.
+template <class CF, class CH, int EPI>
+__global__ __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void wgrad_persistent_kernel(WgradArgs a, int stagger) {
+  static_assert(CF::THREADS == CH::THREADS && CF::BM == CH::BM && CF::BN == 2 * CH::BN,
+                "half tiles must split the full tile's columns");
+  constexpr int LDS = CF::LDS_ELEMS > CH::LDS_ELEMS ? CF::LDS_ELEMS : CH::LDS_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3, nw = gridDim.x >> 3;
+  // This XCD's contiguous range of the grouped tile order.
+  const int per = a.num_tiles >> 3, rem = a.num_tiles & 7;
+  int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  int R = per + (xcd < rem ? 1 : 0);
+  int ng = nw, jj = j, phase = 0;
+  if (stagger == 1) {
+    phase = xcd & 1;
+  } else if (stagger == 2) {
+    ng = nw >> 1;
+    jj = j >> 1;
+    phase = j & 1;
+    const int R0 = (R + 1) >> 1;
+    start += phase ? R0 : 0;
+    R = phase ? R - R0 : R0;
+  }
+  if (phase && R < ng) phase = 0;    // too little work to offset
+  for (int k = 0;; ++k) {
+    int tile, half;
+    if (!schedule_item(k, jj, ng, R, phase, tile, half)) break;
+    int tm, tn;
+    grouped_walk(start + tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+    if (half < 0)
+      wgrad_tile<CF, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, smem);
+    else
+      wgrad_tile<CH, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, 2 * tn + half, smem);
+    __syncthreads();                 // the next tile's prologue reuses the LDS
+  }
+}
+
 // Unfused elementwise optimizers (the HBM-materialising comparison path).
+template <bool EXACT_SQRT>
 __global__ __launch_bounds__(256) void adamw_elementwise_kernel(const float* __restrict__ g,
                                                                 float* __restrict__ W,
                                                                 float* __restrict__ m,
@@ -539,7 +718,7 @@ __global__ __launch_bounds__(256) void adamw_elementwise_kernel(const float* __r
     f32x4_t w = reinterpret_cast<const f32x4_t*>(W)[k];
     f32x4_t mm = reinterpret_cast<const f32x4_t*>(m)[k];
     f32x4_t vv = reinterpret_cast<const f32x4_t*>(v)[k];
-    adamw_vec4(gg, w, mm, vv, c);
+    adamw_vec4<EXACT_SQRT>(gg, w, mm, vv, c);
     reinterpret_cast<f32x4_t*>(W)[k] = w;
     reinterpret_cast<f32x4_t*>(m)[k] = mm;
     reinterpret_cast<f32x4_t*>(v)[k] = vv;
@@ -547,7 +726,7 @@ __global__ __launch_bounds__(256) void adamw_elementwise_kernel(const float* __r
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
     const int64_t k = (n4 << 2) + threadIdx.x;
     float w = W[k], mm = m[k], vv = v[k];
-    adamw_elem(g[k], w, mm, vv, c);
+    adamw_elem<EXACT_SQRT>(g[k], w, mm, vv, c);
     W[k] = w;
     m[k] = mm;
     v[k] = vv;
