@@ -96,15 +96,15 @@ int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s) {
 // Llama-3-8B MLP-down contraction, relative to 256x256) is scaled by how well
 // its tiles fill whole waves of workgroups over the 256 compute units.
 // Makespan, in full-tile times, of the persistent schedule for `tiles` 256x256
-// tiles on `grid` workgroups (stagger mode 1: odd XCDs half a tile behind). A
-// half tile costs 0.6 of a full one (it runs at ~85% of the full tile's rate).
+// tiles on `grid` workgroups (odd XCDs half a tile behind). A half tile costs
+// 0.6 of a full one (it runs at ~85% of the full tile's rate).
 double persistent_makespan(int64_t tiles, int grid) {
   const int nw = grid / 8;
   double worst = 0.0;
   for (int xcd = 0; xcd < 8; ++xcd) {
     const int64_t per = tiles / 8, rem = tiles % 8;
     const int R = int(per + (xcd < rem ? 1 : 0));
-    const int phase = (xcd & 1) && R >= nw ? 1 : 0;
+    const int phase = schedule_phase(xcd, R, nw);
     for (int j = 0; j < nw; ++j) {
       double t = 0.0;
       int tile, half;
@@ -153,7 +153,7 @@ forge_status launch_status() {
 }
 
 // Tile configurations behind the public tile ids.
-using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1, LAYOUT_T>;
+using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 1>;
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 32, 2>;
 
@@ -172,16 +172,13 @@ forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
   return launch_status();
 }
 
-// Stagger mode of the persistent kernel: odd XCDs half a tile behind.
-constexpr int kStagger = 1;
-
 template <int EPI>
 forge_status launch_persistent(WgradArgs a, hipStream_t s) {
   set_grid<Cfg256x256>(a, 1);
   const int grid = persistent_grid();
   if (grid <= 0) return launch_dense_t<Cfg256x256, EPI>(a, s);
   hipLaunchKernelGGL((wgrad_persistent_kernel<Cfg256x256, Cfg256x128, EPI>), dim3(grid),
-                     dim3(Cfg256x256::THREADS), 0, s, a, kStagger);
+                     dim3(Cfg256x256::THREADS), 0, s, a);
   return launch_status();
 }
 

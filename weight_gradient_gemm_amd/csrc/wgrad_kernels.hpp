@@ -10,11 +10,9 @@
 // Mainloop: bf16 MFMA v_mfma_f32_32x32x16_bf16, 4 waves per workgroup, each
 // wave owning a (BM/WAVES_M) x (BN/WAVES_N) block of the tile. Both operands
 // have the token axis strided (X and dY are row-major [T, d]) while an MFMA
-// operand needs 8 consecutive tokens per lane, so every stage of 32 tokens is
-// transposed on its way through LDS: either in registers before the LDS store
-// (LAYOUT_T, one 16-byte LDS read per operand) or by the gfx950 LDS transpose
-// read (LAYOUT_TR). A ring of 3 LDS stages and 3 register sets of global
-// prefetch, one barrier per stage.
+// operand needs 8 consecutive tokens per lane: stages of 32 tokens go from
+// global memory straight into LDS as [token][feature] rows, and the operands
+// are gathered with the gfx950 LDS transpose read (see wgrad_tile).
 //
 // Order of accumulation: for every element, the tokens enter in ascending
 // chunks of 16 through one accumulator, whatever the tile shape or schedule.
@@ -49,7 +47,6 @@ __host__ __device__ constexpr bool is_adamw(int epi) {
   return epi == EPI_ADAMW || epi == EPI_ADAMW_EXACT;
 }
 
-
 struct WgradArgs {
   const uint16_t* X;   // [rows, d_in] bf16 bits
   const uint16_t* dY;  // [rows, d_out] bf16 bits
@@ -72,12 +69,23 @@ struct GroupTable {
   int32_t order[FORGE_MAX_EXPERTS];   // experts in launch order
 };
 
-// Row stride (elements) of an LDS stage holding `w` features per token: padded
-// so that the four token rows read together by a 16-lane transpose read start
-// 64 bytes apart modulo 256 (distinct LDS banks).
-__host__ __device__ constexpr int lds_stride(int w) {
-  return w + ((((w * 2) % 256) == 0) ? 32 : (64 - (w * 2) % 256 + 256) % 256 / 2);
-}
+// Compile-time shape of one workgroup's tile.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int OCC_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_;            // tile extent along d_in, d_out
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int BK = BK_;                      // tokens per LDS stage
+  static constexpr int OCC = OCC_;                    // workgroups per CU the resources allow
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA blocks per wave
+  static constexpr int STAGE = BK * (BM + BN);        // bf16 elements of one LDS stage
+  static_assert(WAVES == 4 && BK == 32, "4 waves, stages of two 16-token MFMA chunks");
+  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA block");
+  static_assert(BM % 128 == 0 && BN % 128 == 0 && BM <= 512 && BN <= 512,
+                "rows of 16 to 64 chunks of 16 bytes");
+};
 
 // Tile grid position of logical tile t of the grouped walk (see map_tile).
 __host__ __device__ inline void grouped_walk(int t, int tiles_m, int tiles_n, int group_m, int& tm,
@@ -131,73 +139,12 @@ __device__ __forceinline__ void sgdm_vec4(const f32x4_t& g, f32x4_t& w, f32x4_t&
   }
 }
 
-// MFMA operand for a 32-wide feature block at column c0 and the 16 tokens
-// starting at row k0 of an LDS stage [token][feature] with row stride LD:
-// lane l gets features c0 + (l % 32), tokens k0 + 8 (l / 32) + 0..7.
-// Two transpose reads, each giving 4 tokens: within a group of 16 lanes, lane
-// j supplies the address of 4 consecutive features of token row j / 4 and
-// receives feature j of each of the group's 4 rows.
-template <int LD>
-__device__ __forceinline__ bf16x8_t load_operand(const uint16_t* s, int k0, int c0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = k0 + 8 * (g >> 1) + (j >> 2);
-  const int col = c0 + 16 * (g & 1) + 4 * (j & 3);
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const uint16_t* p0 = s + row * LD + col;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * LD));
-  const i16x4_t both[2] = {lo, hi};
-  bf16x8_t r;
-  __builtin_memcpy(&r, both, sizeof(r));
-  return r;
-}
-
-// Compile-time shape of one workgroup's tile and its LDS stage.
-// LDS layouts of a stage.
-//   LAYOUT_TR: [token][feature] rows as loaded (padded); MFMA operands are
-//              gathered with the LDS transpose read (two 8-byte reads each).
-//   LAYOUT_T:  [feature][token] 16-byte cells of 8 tokens, transposed in
-//              registers on the way in; an MFMA operand is one 16-byte read.
-enum Layout : int { LAYOUT_TR = 0, LAYOUT_T = 1 };
-
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int OCC_, int LAYOUT_ = LAYOUT_TR>
-struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_;            // tile extent along d_in, d_out
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int BK = BK_;                      // tokens per LDS stage
-  static constexpr int OCC = OCC_;                    // workgroups per CU the registers allow
-  static constexpr int WAVES = WAVES_M * WAVES_N;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA blocks per wave
-  static constexpr int LAYOUT = LAYOUT_;
-  static constexpr int LDX = LAYOUT == LAYOUT_TR ? lds_stride(BM) : BM;
-  static constexpr int LDY = LAYOUT == LAYOUT_TR ? lds_stride(BN) : BN;
-  static constexpr int STAGE = BK * (LDX + LDY);      // elements of one LDS stage
-  static constexpr int XPT = BK * BM / 8 / THREADS;   // 16-byte global chunks per thread
-  static constexpr int YPT = BK * BN / 8 / THREADS;
-  // LAYOUT_T: each thread loads one block of 8 tokens x 8 features.
-  static constexpr int XBLK = (BM / 8) * (BK / 8), YBLK = (BN / 8) * (BK / 8);
-  static constexpr int NLOAD = LAYOUT == LAYOUT_TR ? XPT + YPT : 8;
-  static constexpr int STAGES = 3;                    // LDS ring depth
-  // The epilogue reuses the ring: per wave 32 rows of WM + 4 floats.
-  static constexpr int EPI_ELEMS = WAVES * 32 * (WM + 4) * 2;
-  static constexpr int LDS_ELEMS = STAGES * STAGE > EPI_ELEMS ? STAGES * STAGE : EPI_ELEMS;
-  static constexpr int NFRAG = TM + TN;               // MFMA operands per wave per chunk
-  static_assert(BK % 16 == 0, "stage must hold whole MFMA token chunks");
-  static_assert(LAYOUT != LAYOUT_TR ||
-                    (XPT * THREADS * 8 == BK * BM && YPT * THREADS * 8 == BK * BN),
-                "stage not evenly split over threads");
-  static_assert(LAYOUT != LAYOUT_T || (XBLK + YBLK == THREADS && XBLK % 64 == 0),
-                "transposed layout needs one block per thread, X blocks on whole waves");
-  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA block");
-};
-
 // Byte offset that lies beyond every buffer window: the hardware returns zeros.
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Raw buffer window over `bytes` bytes from `base` (reads at or past the end
-// return 0). Word 3 is the gfx9-family raw-buffer format.
+// return 0, writes there are dropped). Word 3 is the gfx9-family raw-buffer
+// format.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > int64_t(kOOB) ? int64_t(kOOB) : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
@@ -209,65 +156,85 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window32(const void* base, uin
                                            0x00020000);
 }
 
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-#ifndef FORGE_EPI_UNIT
-#define FORGE_EPI_UNIT 4      // row instructions per epilogue unit
-#endif
-#ifndef FORGE_EPI_DEPTH
-#define FORGE_EPI_DEPTH 2     // units whose state loads are in flight together
-#endif
-#ifndef FORGE_EPI_AUX
-#define FORGE_EPI_AUX 0       // cache policy of the state loads and stores
-#endif
+// Optimizer state is streamed once per step: non-temporal cache policy.
+constexpr int kStatePolicy = 2;
 
 __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                         const f32x4_t& v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)voff, (int)soff,
-                                         FORGE_EPI_AUX);
+                                         kStatePolicy);
 }
 
 __device__ __forceinline__ f32x4_t load16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(
-      f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, FORGE_EPI_AUX));
+      f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kStatePolicy));
 }
 
-// Row-major epilogue through LDS (see wgrad_tile). Each wave owns a region of
-// 32 rows x (WM + 4) floats; the 4-float pad keeps both the column-major dump
-// (16 rows per 256 bytes of banks) and the row-major read conflict-free.
+// s_waitcnt immediate (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4 (left at its maximum), lgkmcnt in 11:8.
+__host__ __device__ constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
+
+__host__ __device__ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// 16 bytes per lane from a buffer window straight into LDS: lane t writes at
+// dst + 16 t (dst is wave-uniform; it becomes M0).
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint16_t* dst,
+                                              uint32_t voff, int soff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+
+// LDS transpose read of 4 x 16-bit values (see wgrad_tile).
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// The four LDS ring slots of a workgroup. Each is its own __shared__ array,
+// which lets the compiler tell the slots apart when it places waits for the
+// direct-to-LDS loads.
+struct Slots {
+  uint16_t *s0, *s1, *s2, *s3;
+};
+
+// Row-major epilogue through LDS. Each wave owns a region of 32 rows x
+// (WM + 4) floats (in one of the ring slots); the 4-float pad keeps both the
+// column-major dump and the row-major read conflict-free. A direct store from
+// the MFMA result layout would touch 32 rows of W per instruction; after the
+// pass through LDS every state access covers 256 / WM whole rows of WM
+// contiguous floats.
 //
-// The wave's 32-column blocks are cut into units of FORGE_EPI_UNIT row
-// instructions and software-pipelined: the state loads of the next
-// FORGE_EPI_DEPTH - 1 units are issued before a unit's optimizer math and
-// stores, so memory latency overlaps the arithmetic. (On this chip family
-// the vector-memory counter covers stores as well as loads and drains in
-// issue order, so loads issued after a unit's stores would also wait for
-// those stores; issuing them first keeps the stores in flight.) State is
-// addressed through buffer windows of one 32-row block: rows past d_out lie
-// beyond the window (loads read 0, stores are dropped) and columns past d_in
-// get an out-of-window lane offset, so no lane needs a branch.
+// The wave's 32-column blocks are cut into units of 4 row instructions and
+// software-pipelined: the next unit's state loads are issued before a unit's
+// optimizer math and stores, so memory latency overlaps the arithmetic. (On
+// this chip family the vector-memory counter covers stores as well as loads
+// and drains in issue order, so loads issued after a unit's stores would also
+// wait for those stores; issuing them first keeps the stores in flight.)
+// State is addressed through buffer windows of one 32-row block: rows past
+// d_out lie beyond the window (loads read 0, stores are dropped) and columns
+// past d_in get an out-of-window lane offset, so no lane needs a branch.
 template <class C, int EPI>
 __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::TM][C::TN],
                                          float* __restrict__ W, float* __restrict__ S1,
                                          float* __restrict__ S2, int i0, int o0, int wm, int wn,
-                                         int lane, int wave, uint16_t* smem) {
+                                         int lane, float* ep) {
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM;
   constexpr int LD = WM + 4;                 // floats per LDS row
   constexpr int LPR = WM / 4;                // lanes per row (float4 each)
   constexpr int RPI = 64 / LPR;              // rows per instruction
   constexpr int NI = 32 / RPI;               // instructions per 32-column block
-  constexpr int B = NI < FORGE_EPI_UNIT ? NI : FORGE_EPI_UNIT;
+  constexpr int B = NI < 4 ? NI : 4;         // instructions per unit
   constexpr int UPB = NI / B;                // units per block
   constexpr int U = TN * UPB;
-  constexpr int D = FORGE_EPI_DEPTH;
+  constexpr int D = 2;                       // units in flight
   constexpr int NS = is_adamw(EPI) ? 3 : (EPI == EPI_SGDM ? 2 : 0);   // state arrays read
-  static_assert(NI % B == 0 && D >= 1, "epilogue units must tile a block");
-  static_assert(C::WAVES * 32 * LD * 4 <= C::LDS_ELEMS * 2, "epilogue staging exceeds LDS");
+  static_assert(NI % B == 0, "epilogue units must tile a block");
+  static_assert(32 * LD * 4 <= C::STAGE * 2, "a wave's epilogue staging exceeds a slot");
+
   const int d_in = a.d_in, d_out = a.d_out;
   __syncthreads();                           // every wave is done with the operand ring
-  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LD;
   const int r_lane = lane / LPR, c_lane = (lane % LPR) * 4;
   const int iw0 = i0 + wm * WM;
   const uint32_t voff = iw0 + c_lane < d_in ? uint32_t(r_lane * d_in + c_lane) * 4u : kOOB;
@@ -339,156 +306,126 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   }
 }
 
+// One output tile: mainloop over all tokens, then the epilogue.
+//
+// Staging: a buffer load with the LDS flag writes lane t's 16 bytes at
+// M0 + 16 t (lanes whose offset falls outside the buffer window write zeros),
+// so the operands reach LDS without passing through registers, permutes or
+// LDS store instructions. A stage holds [token][feature] rows of X, then of
+// dY; the 16-byte chunk c of token row r is stored at chunk c ^ 4 (r mod 4).
+// An MFMA operand (8 consecutive tokens of one feature per lane) is gathered
+// with two LDS transpose reads (ds_read_b64_tr_b16): within a group of 16
+// lanes, lane j supplies the address of 4 consecutive features of token row
+// j / 4 and receives feature j of each of the group's 4 rows. Each 32-lane
+// half of such a read touches 4 rows x 64 contiguous bytes; the swizzle puts
+// the 4 rows on disjoint banks.
+//
+// Ring of 4 slots. Per stage s (two 16-token chunks):
+//   chunk 0: MFMAs on chunk 0; read chunk 1's operands from slot s % 4.
+//   wait for this wave's LDS reads (slot s % 4 is then free) and for its
+//   loads of stage s + 1; barrier (no fence: the waits are explicit).
+//   chunk 1: load stage s + 4 into slot s % 4; MFMAs on chunk 1; read stage
+//   s + 1's chunk 0 operands from slot (s + 1) % 4.
+// Each load has about two and a half stages of MFMA work to land.
 template <class C, int EPI>
 __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* __restrict__ X,
                                            const uint16_t* __restrict__ dY,
                                            float* __restrict__ W, float* __restrict__ S1,
                                            float* __restrict__ S2, int64_t T, int tile_m,
-                                           int tile_n, uint16_t* smem) {
+                                           int tile_n, const Slots& sl) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
-  constexpr int LDX = C::LDX, LDY = C::LDY, STAGE = C::STAGE, XPT = C::XPT, YPT = C::YPT;
-  constexpr int NT = C::THREADS;
+  constexpr int RBX = BM * 2, RBY = BN * 2;             // bytes per token row
+  constexpr int CPX = BM / 8, CPY = BN / 8;             // 16-byte chunks per row
+  constexpr int QX = BK * RBX / 1024, QY = BK * RBY / 1024;
+  constexpr int NQW = (QX + QY) / C::WAVES;             // 1 KB loads per wave per stage
+  constexpr int L = 4;                                  // ring slots
+  static_assert((QX + QY) % C::WAVES == 0, "stage loads split evenly over the waves");
 
   // The wave index is uniform; readfirstlane lets the compiler keep what
-  // derives from it (buffer windows, tile offsets) in scalar registers.
+  // derives from it (buffer windows, LDS bases, tile offsets) scalar.
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int d_in = a.d_in, d_out = a.d_out;
   const int i0 = tile_m * BM, o0 = tile_n * BN;
 
-  struct Regs {
-    u32x4_t r[C::NLOAD];
-  };
-  // Operand registers: two sets, alternating between consecutive 16-token
-  // chunks. Set f holds TM operands of X^T then TN operands of dY.
-  bf16x8_t frag[2][C::NFRAG];
-
-  // ---- LAYOUT_TR: thread's chunks of a stage: chunk c = tid + NT q is token
-  // row c / (W/8) of the stage, features (c % (W/8)) * 8 .. + 7. Feature
-  // chunks past d read as zero (offset kOOB); token rows past T fall outside
-  // the stage window.
-  uint32_t c_off[C::LAYOUT == LAYOUT_TR ? XPT + YPT : 1];
-  int c_lds[C::LAYOUT == LAYOUT_TR ? XPT + YPT : 1];
-  // ---- LAYOUT_T: thread owns block (chunk, tg): features 8 chunk .. + 7 of X
-  // (waves holding the first XBLK threads) or dY, tokens 8 tg .. + 7 of the
-  // stage. Cell (f, tg) of an operand region sits at 16-byte slot
-  //   16 (TG (f / 16) + tg) + b(f, tg),
-  //   b = (f mod 8) ^ ((f / 8) mod 8) ^ 8 ((f / 8) mod 2) ^ 8 (tg mod 2),
-  // a GF(2)-linear bank map. Measured on gfx950, 16-byte LDS reads are
-  // serviced in 16-lane groups {0-7, 24-31}, {8-15, 16-23}, ... over 16 bank
-  // groups and 16-byte writes in groups of 8 consecutive lanes over 8 bank
-  // groups; b keeps the MFMA reads (features c0 + lane % 32) and the
-  // transposed writes (features 8 (lane % 32) + j) free of bank conflicts
-  // under those rules (and under plain 16-lane groups), checked exhaustively.
-  const bool t_is_x = C::LAYOUT == LAYOUT_T && wave < C::XBLK / 64;
-  const int t_blk = t_is_x ? tid : tid - C::XBLK;
-  const int t_nch = t_is_x ? BM / 8 : BN / 8;
-  const int t_chunk = t_blk % t_nch, t_tg = t_blk / t_nch;
-  const int t_dim = t_is_x ? d_in : d_out;
-  const int t_c0 = t_is_x ? i0 : o0;
-  const uint16_t* t_src = t_is_x ? X : dY;
-  const int t_region = t_is_x ? 0 : BK * LDX;   // element offset of the operand region
-  const uint32_t t_voff = t_c0 + 8 * t_chunk < t_dim
-                              ? uint32_t(8 * t_tg * t_dim + 8 * t_chunk) * 2u : kOOB;
-  auto cell = [](int f, int tg) {
-    constexpr int TG = BK / 8;
-    const int b = (f & 7) ^ ((f >> 3) & 7) ^ (((f >> 3) & 1) << 3) ^ ((tg & 1) << 3);
-    return 8 * (16 * (TG * (f >> 4) + tg) + b);   // in elements
-  };
-
-  if constexpr (C::LAYOUT == LAYOUT_TR) {
+  // This wave's loads of a stage: instruction i is q = NQW wave + i over the
+  // stage's X rows then dY rows, 64 / (chunks per row) rows each.
+  uint32_t voff[NQW];
+  int soff[NQW];
 #pragma unroll
-    for (int q = 0; q < XPT; ++q) {
-      const int c = tid + NT * q, r = c / (BM / 8), col = (c % (BM / 8)) * 8;
-      c_lds[q] = r * LDX + col;
-      c_off[q] = i0 + col < d_in ? uint32_t(r * d_in + col) * 2u : kOOB;
-    }
-#pragma unroll
-    for (int q = 0; q < YPT; ++q) {
-      const int c = tid + NT * q, r = c / (BN / 8), col = (c % (BN / 8)) * 8;
-      c_lds[XPT + q] = BK * LDX + r * LDY + col;
-      c_off[XPT + q] = o0 + col < d_out ? uint32_t(r * d_out + col) * 2u : kOOB;
-    }
+  for (int i = 0; i < NQW; ++i) {
+    const int q = wave * NQW + i;
+    const bool isx = q < QX;
+    const int sh = isx ? ilog2(CPX) : ilog2(CPY);
+    const int dim = isx ? d_in : d_out, c0 = isx ? i0 : o0;
+    const int row0 = (isx ? q : q - QX) << (6 - sh);
+    const int lrow = lane >> sh, p = lane & ((1 << sh) - 1);
+    const int ch = p ^ (4 * ((row0 + lrow) & 3));
+    voff[i] = c0 + 8 * ch < dim ? uint32_t(lrow * dim + 8 * ch) * 2u : kOOB;
+    soff[i] = row0 * dim * 2;
   }
-
   // Stage loads walk the token axis in order with running pointers. The
   // window of stage s covers only its own token rows (BK, the tail, or none),
-  // so rows past T read as zero; its size fits 32 bits and takes a few
-  // scalar instructions per stage.
+  // so rows past T read as zero; its size fits 32 bits.
   const int nfull = int(T / BK), tail = int(T - int64_t(nfull) * BK);
   int g_stage = 0;
-  const uint16_t* g_x = X + i0;                  // LAYOUT_TR
-  const uint16_t* g_y = dY + o0;
-  const int t_dim_s = __builtin_amdgcn_readfirstlane(t_dim);
-  const uint16_t* g_s = t_src + t_c0;            // LAYOUT_T
+  const uint16_t* gx = X + i0;
+  const uint16_t* gy = dY + o0;
   auto stage_bytes = [&](int dim, int c0) {
     const int rows = g_stage < nfull ? BK : (g_stage == nfull ? tail : 0);
     const int n = rows * dim - c0;               // c0 >= dim: a tile past the edge
     return n > 0 ? uint32_t(n) * 2u : 0u;
   };
-  auto gload = [&](Regs& R) {
-    if constexpr (C::LAYOUT == LAYOUT_TR) {
-      const __amdgpu_buffer_rsrc_t rx = window32(g_x, stage_bytes(d_in, i0));
-      const __amdgpu_buffer_rsrc_t ry = window32(g_y, stage_bytes(d_out, o0));
-      g_x += BK * d_in;
-      g_y += BK * d_out;
-      ++g_stage;
+  auto load_stage = [&](uint16_t* slot) {
+    const __amdgpu_buffer_rsrc_t rx = window32(gx, stage_bytes(d_in, i0));
+    const __amdgpu_buffer_rsrc_t ry = window32(gy, stage_bytes(d_out, o0));
+    gx += BK * d_in;
+    gy += BK * d_out;
+    ++g_stage;
 #pragma unroll
-      for (int q = 0; q < XPT; ++q) R.r[q] = load16(rx, c_off[q]);
-#pragma unroll
-      for (int q = 0; q < YPT; ++q) R.r[XPT + q] = load16(ry, c_off[XPT + q]);
-    } else {
-      const int dim = t_dim_s;
-      const __amdgpu_buffer_rsrc_t rs = window32(g_s, stage_bytes(dim, t_c0));
-      g_s += BK * dim;
-      ++g_stage;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        R.r[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, (int)t_voff, j * dim * 2, 0));
+    for (int i = 0; i < NQW; ++i) {
+      const int q = wave * NQW + i;
+      load16_to_lds(q < QX ? rx : ry, slot + q * 512, voff[i], soff[i]);
     }
   };
-  auto sstore = [&](const Regs& R, int buf) {
-    uint16_t* st = smem + buf * STAGE;
-    if constexpr (C::LAYOUT == LAYOUT_TR) {
+
+  // Transpose-read addresses (bytes within a slot) of this lane's operands:
+  // lane j of 16-lane group g reads 4 features of token row 8 (g / 2) + j / 4
+  // (+ 16 for chunk 1, + 4 for the second read of an operand) at chunk
+  // 4 blk + 2 (g % 2) + (j % 4) / 2 of the operand's 32-feature block blk.
+  const int g = lane >> 4, j = lane & 15;
+  const int rsub = 8 * (g >> 1) + (j >> 2);
+  uint32_t fa[TM], fb[TN];
 #pragma unroll
-      for (int q = 0; q < XPT + YPT; ++q) *reinterpret_cast<u32x4_t*>(st + c_lds[q]) = R.r[q];
-    } else {
-      // 8x8 transpose of bf16: output f holds tokens 0..7 of feature 8 chunk + f;
-      // its dword i packs tokens 2i (low half) and 2i+1 from input rows 2i, 2i+1.
+  for (int m = 0; m < TM; ++m) {
+    const int blk = (wm * C::WM + m * 32) >> 5;
+    const int ch = (4 * blk + 2 * (g & 1) + ((j & 3) >> 1)) ^ (4 * (j >> 2));
+    fa[m] = uint32_t(rsub * RBX + ch * 16 + (j & 1) * 8);
+  }
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = __builtin_amdgcn_perm(R.r[2 * i + 1][f >> 1], R.r[2 * i][f >> 1], sel);
-        *reinterpret_cast<u32x4_t*>(st + t_region + cell(8 * t_chunk + f, t_tg)) = o;
-      }
-    }
+  for (int n = 0; n < TN; ++n) {
+    const int blk = (wn * C::WN + n * 32) >> 5;
+    const int ch = (4 * blk + 2 * (g & 1) + ((j & 3) >> 1)) ^ (4 * (j >> 2));
+    fb[n] = uint32_t(BK * RBX + rsub * RBY + ch * 16 + (j & 1) * 8);
+  }
+  auto operand = [](const uint16_t* slot, uint32_t off, int rb) {
+    const char* b = reinterpret_cast<const char*>(slot) + off;
+    const i16x4_t lo = lds_read_tr16(b);
+    const i16x4_t hi = lds_read_tr16(b + 4 * rb);
+    const i16x4_t both[2] = {lo, hi};
+    bf16x8_t r;
+    __builtin_memcpy(&r, both, sizeof(r));
+    return r;
   };
-  auto read_frags = [&](int f, int buf, int kk) {
-    const uint16_t* sx = smem + buf * STAGE;
-    const uint16_t* sy = sx + BK * LDX;
-    if constexpr (C::LAYOUT == LAYOUT_TR) {
+  // Operand registers: two sets, alternating between consecutive 16-token
+  // chunks. Set f holds TM operands of X^T then TN operands of dY.
+  bf16x8_t frag[2][TM + TN];
+  auto read_frags = [&](int f, const uint16_t* slot, int kk) {
 #pragma unroll
-      for (int m = 0; m < TM; ++m)
-        frag[f][m] = load_operand<LDX>(sx, kk, wm * C::WM + m * 32, lane);
+    for (int m = 0; m < TM; ++m) frag[f][m] = operand(slot, fa[m] + kk * 16 * RBX, RBX);
 #pragma unroll
-      for (int n = 0; n < TN; ++n)
-        frag[f][TM + n] = load_operand<LDY>(sy, kk, wn * C::WN + n * 32, lane);
-    } else {
-      const int tg = kk / 8 + (lane >> 5);
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-        frag[f][m] = *reinterpret_cast<const bf16x8_t*>(
-            sx + cell(wm * C::WM + m * 32 + (lane & 31), tg));
-#pragma unroll
-      for (int n = 0; n < TN; ++n)
-        frag[f][TM + n] = *reinterpret_cast<const bf16x8_t*>(
-            sy + cell(wn * C::WN + n * 32 + (lane & 31), tg));
-    }
+    for (int n = 0; n < TN; ++n) frag[f][TM + n] = operand(slot, fb[n] + kk * 16 * RBY, RBY);
   };
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -497,7 +434,6 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
     for (int n = 0; n < TN; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-
   auto mfmas = [&](int f) {
 #pragma unroll
     for (int m = 0; m < TM; ++m)
@@ -506,94 +442,82 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
         acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[f][m], frag[f][TM + n],
                                                             acc[m][n], 0, 0, 0);
   };
-  // Interleave one MFMA with the other instruction groups of a chunk so the
-  // matrix core never waits on an issue slot: `reads` LDS reads, `loads`
-  // global loads and `writes` LDS writes spread over the chunk's MFMAs.
-  auto interleave = [&](int reads, int loads, int writes) {
+  // Interleave each MFMA with up to two transpose reads and one stage load so
+  // the matrix core keeps issuing while LDS and memory work proceed.
+  constexpr int NREAD = 2 * (TM + TN);
+  auto interleave = [&](int loads) {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-      if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-      if (i < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
-      if (i >= TM * TN - writes) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+      if (i < NREAD / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read
+      if (i < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // VMEM read
     }
   };
-
-  // Mainloop over stages of BK tokens: an LDS ring of 3 stages and 3 register
-  // sets of global prefetch. At the top of stage s, LDS[s % 3] and
-  // LDS[(s+1) % 3] hold stages s and s+1 (published by earlier barriers),
-  // frag[0] holds stage s's first chunk, and the register sets hold stages
-  // s+2 and s+3 (in flight). During stage s:
-  //   - stage s+4 is requested into the set that held stage s+1;
-  //   - the chunks' operands are read one chunk ahead from LDS (the last
-  //     chunk reads stage s+1's first chunk);
-  //   - stage s+2 is written to LDS[(s+2) % 3], the buffer of stage s-1,
-  //     which every wave finished before the previous barrier.
-  // So each global load has about three stages of MFMA work to land. One
-  // barrier per stage publishes the write. Stages past the end are fetched
-  // through an empty window (zeros) into buffers nobody reads again, which
-  // keeps each stage one straight-line scheduling region.
-  constexpr int KK = BK / 16;
-  // LDS reads per chunk; global loads and LDS writes per stage.
-  constexpr int NREAD = C::LAYOUT == LAYOUT_TR ? 2 * C::NFRAG : C::NFRAG;
-  constexpr int NLOAD = C::NLOAD;
-  static_assert(KK % 2 == 0, "the operand-set alternation assumes an even chunk count");
+  // The barrier orders LDS traffic between waves; the waits before it are
+  // explicit, so neither the compiler nor the scheduler may move memory
+  // operations across it.
+  constexpr int kWaitMid = waitcnt_imm((L - 2) * NQW, 0);
+  constexpr int kWaitFirst = waitcnt_imm((L - 1) * NQW, 15);
+#define FORGE_STAGE_BARRIER(IMM)              \
+  do {                                        \
+    __builtin_amdgcn_sched_barrier(0);        \
+    __builtin_amdgcn_s_waitcnt(IMM);          \
+    asm volatile("" ::: "memory");            \
+    __builtin_amdgcn_s_barrier();             \
+    asm volatile("" ::: "memory");            \
+    __builtin_amdgcn_sched_barrier(0);        \
+  } while (0)
+  auto stage = [&](uint16_t* cur, uint16_t* nxt) {
+    read_frags(1, cur, 1);
+    mfmas(0);
+    interleave(0);
+    FORGE_STAGE_BARRIER(kWaitMid);
+    load_stage(cur);                             // stage s + 4 into the freed slot
+    read_frags(0, nxt, 0);
+    mfmas(1);
+    interleave(NQW);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   const int nk = int((T + BK - 1) / BK);
-  auto stage = [&](Regs& r_load, const Regs& r_store, int buf, int buf1, int buf2) {
-    gload(r_load);                               // stage s + 4 during stage s
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int f = kk & 1;
-      if (kk < KK - 1) {
-        read_frags(f ^ 1, buf, (kk + 1) * 16);
-      } else {
-        read_frags(f ^ 1, buf1, 0);
-      }
-      mfmas(f);
-      if (kk == KK - 1) sstore(r_store, buf2);
-      interleave(NREAD, kk == 0 ? NLOAD : 0, kk == KK - 1 ? NLOAD : 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-  };
   if (nk > 0) {
-    Regs r0, r1, r2;
-    gload(r0);
-    gload(r1);
-    gload(r2);
-    sstore(r0, 0);
-    sstore(r1, 1);
-    __syncthreads();
-    gload(r0);
-    read_frags(0, 0, 0);
-    // Whole rounds of 3 stages keep one loop exit (so the accumulators keep
-    // their registers). Up to two extra stages read zeros: a chunk of zero
+    load_stage(sl.s0);
+    load_stage(sl.s1);
+    load_stage(sl.s2);
+    load_stage(sl.s3);
+    FORGE_STAGE_BARRIER(kWaitFirst);
+    read_frags(0, sl.s0, 0);
+    // Whole rounds of 4 stages keep one loop exit (so the accumulators keep
+    // their registers). Up to three extra stages load zeros: a chunk of zero
     // products adds exactly +0 to an accumulator that is never -0 (it starts
     // at +0 and an exact-zero sum rounds to +0), so they change no bit.
-    const int rounds = (nk + 2) / 3;
+    const int rounds = (nk + L - 1) / L;
     for (int r = 0; r < rounds; ++r) {
-      stage(r1, r2, 0, 1, 2);
-      stage(r2, r0, 1, 2, 0);
-      stage(r0, r1, 2, 0, 1);
+      stage(sl.s0, sl.s1);
+      stage(sl.s1, sl.s2);
+      stage(sl.s2, sl.s3);
+      stage(sl.s3, sl.s0);
     }
   }
-
-  // Epilogue. The MFMA result gives each lane 4-row pieces of one column, so a
-  // direct store touches 32 rows of W per instruction. Instead, each wave
-  // passes its accumulators through LDS one 32-column block at a time and
-  // reads them back row-major: every global instruction then covers
-  // 256 / WM whole rows of WM contiguous floats of W (and of m, v). Loads of
-  // EPI_BATCH instructions are in flight before any optimizer math.
-  epilogue<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, wave, smem);
+#undef FORGE_STAGE_BARRIER
+  // The epilogue starts with a full barrier, which also waits for the loads
+  // of the zero stages still in flight.
+  uint16_t* ep = wave == 0 ? sl.s0 : wave == 1 ? sl.s1 : wave == 2 ? sl.s2 : sl.s3;
+  epilogue<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, reinterpret_cast<float*>(ep));
 }
+
+// The ring slots of a kernel, sized for its largest tile.
+#define FORGE_DECLARE_SLOTS(ELEMS)                                                         \
+  __shared__ __attribute__((aligned(1024))) uint16_t forge_s0[ELEMS], forge_s1[ELEMS],     \
+      forge_s2[ELEMS], forge_s3[ELEMS];                                                    \
+  const Slots ring{forge_s0, forge_s1, forge_s2, forge_s3}
 
 template <class C, int EPI>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void wgrad_dense_kernel(WgradArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  FORGE_DECLARE_SLOTS(C::STAGE);
   int e, tm, tn;
   map_tile(blockIdx.x, a.num_tiles, a.tiles_m, a.tiles_n, a.group_m, e, tm, tn);
-  wgrad_tile<C, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, smem);
+  wgrad_tile<C, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, ring);
 }
 
 // Routed experts: the grid is laid out expert-major in the order of
@@ -602,7 +526,7 @@ void wgrad_dense_kernel(WgradArgs a) {
 template <class C, int EPI>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  FORGE_DECLARE_SLOTS(C::STAGE);
   const int per_expert = a.tiles_m * a.tiles_n;
   const int slot = blockIdx.x / per_expert;
   const int e = gt.order[slot];
@@ -612,7 +536,7 @@ void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
   const int64_t r0 = gt.off[e], r1 = gt.off[e + 1];
   const int64_t state = int64_t(e) * a.d_out * a.d_in;
   wgrad_tile<C, EPI>(a, a.X + r0 * a.d_in, a.dY + r0 * a.d_out, a.W + state, a.S1 + state,
-                     a.S2 + state, r1 - r0, tm, tn, smem);
+                     a.S2 + state, r1 - r0, tm, tn, ring);
 }
 
 // Persistent schedule. One workgroup per CU walks a list of items, each a full
@@ -660,49 +584,44 @@ __host__ __device__ inline bool schedule_item(int k, int j, int ng, int R, int p
   return true;
 }
 
+// The phase of XCD `xcd` holding R tiles for ng workers: odd XCDs run half a
+// tile behind when every worker has at least one full tile.
+__host__ __device__ inline int schedule_phase(int xcd, int R, int ng) {
+  return (xcd & 1) && R >= ng ? 1 : 0;
+}
+
 // Persistent dense kernel over the schedule above. The grid is 8 * nw
-// workgroups (nw per XCD, even). Stagger mode 1: each XCD is a group of nw
-// workers, odd XCDs in phase 1. Mode 2: each XCD holds two groups of nw / 2
-// (even and odd workers), the odd group in phase 1. Mode 0: one group per XCD,
-// all in phase 0. Full tiles use CF, half tiles CH (same BM and threads, half
-// the BN); each element still takes its tokens in ascending 16-token chunks
-// through one accumulator, so the result is bitwise that of any other tiling.
+// workgroups (nw per XCD, even); each XCD is one group of nw workers over its
+// contiguous range of the grouped tile order. Full tiles use CF, half tiles
+// CH (same BM and threads, half the BN); each element still takes its tokens
+// in ascending 16-token chunks through one accumulator, so the result is
+// bitwise that of any other tiling.
 template <class CF, class CH, int EPI>
 __global__ __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void wgrad_persistent_kernel(WgradArgs a, int stagger) {
+void wgrad_persistent_kernel(WgradArgs a) {
   static_assert(CF::THREADS == CH::THREADS && CF::BM == CH::BM && CF::BN == 2 * CH::BN,
                 "half tiles must split the full tile's columns");
-  constexpr int LDS = CF::LDS_ELEMS > CH::LDS_ELEMS ? CF::LDS_ELEMS : CH::LDS_ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
+  FORGE_DECLARE_SLOTS(CF::STAGE);
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3, nw = gridDim.x >> 3;
   // This XCD's contiguous range of the grouped tile order.
   const int per = a.num_tiles >> 3, rem = a.num_tiles & 7;
-  int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  int R = per + (xcd < rem ? 1 : 0);
-  int ng = nw, jj = j, phase = 0;
-  if (stagger == 1) {
-    phase = xcd & 1;
-  } else if (stagger == 2) {
-    ng = nw >> 1;
-    jj = j >> 1;
-    phase = j & 1;
-    const int R0 = (R + 1) >> 1;
-    start += phase ? R0 : 0;
-    R = phase ? R - R0 : R0;
-  }
-  if (phase && R < ng) phase = 0;    // too little work to offset
+  const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  const int R = per + (xcd < rem ? 1 : 0);
+  const int phase = schedule_phase(xcd, R, nw);
   for (int k = 0;; ++k) {
     int tile, half;
-    if (!schedule_item(k, jj, ng, R, phase, tile, half)) break;
+    if (!schedule_item(k, j, nw, R, phase, tile, half)) break;
     int tm, tn;
     grouped_walk(start + tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
     if (half < 0)
-      wgrad_tile<CF, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, smem);
+      wgrad_tile<CF, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, tn, ring);
     else
-      wgrad_tile<CH, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, 2 * tn + half, smem);
-    __syncthreads();                 // the next tile's prologue reuses the LDS
+      wgrad_tile<CH, EPI>(a, a.X, a.dY, a.W, a.S1, a.S2, a.T, tm, 2 * tn + half, ring);
+    __syncthreads();                 // the next tile's loads reuse the slots
   }
 }
+
+#undef FORGE_DECLARE_SLOTS
 
 // Unfused elementwise optimizers (the HBM-materialising comparison path).
 template <bool EXACT_SQRT>
