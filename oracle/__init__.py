@@ -14,22 +14,32 @@ ships AdamW and SGD only). Fusion changes where the gradient lives, not its
 value (section "Math verified, not asserted", P1), so the unfused definition
 is the reference for the fused kernels.
 
+The precision variants of P6 (a bf16-rounded gradient, bf16 moments) and the
+float64 reference they are measured against are in ``ref.py`` too; the P6
+study itself in ``precision_study.py``.
+
 Parity pins (tests that check this package against closed forms, exact
-rational arithmetic and invariants) live in tests/test_oracle_pins.py.
+rational arithmetic and invariants) live in tests/test_oracle_pins.py and
+tests/test_precision_oracle.py.
 Parity unpinned: the exact summation order inside the GPU contraction (only
 the accumulation floor in ``floor.py`` bounds it), and the magnitudes the page
-quotes without their setups (2.24x at 50% routing, ~900x / ~1x).
+quotes without their setups (2.24x at 50% routing; ~900x / ~1x, which the
+study reproduces under a stated reading of the error measure).
 """
 from .ref import (  # noqa: F401
     ClipNotFusable,
     adamw_moments,
     adamw_param,
     adamw_step,
+    adamw_step_f64,
+    adamw_step_mixed,
     bf16_bits_to_f64,
+    bf16_round,
     grouped_adamw_step,
     grouped_wgrad,
     sgdm_step,
     wgrad,
+    wgrad_f64,
     wgrad_rows,
 )
 from .floor import StateFloor, acc_floor, acc_floor_rows  # noqa: F401

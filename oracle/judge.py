@@ -29,6 +29,23 @@ Accuracy bar (per element, every step):
   * epilogue consistency (AdamW): the oracle's float32 parameter update
     applied to the GPU's own W_{t-1}, m_t, v_t must land within 1e-3 lr of the
     GPU's W_t, on every element.
+
+Precision variants (bf16 gradient and/or bf16 moments; judge_adamw_mixed):
+each step is judged from the same state on both sides (the GPU's previous
+W, m, v), so the only input difference is the float32 accumulation floor tau.
+  * bf16 gradient: rounding is monotone, so the GPU's rounded gradient lies
+    between the roundings of g_ref - tau and g_ref + tau; the floor becomes
+    the distance from the oracle's rounded gradient to the farther of the two.
+  * moments: the float32 bar above plus the rounding of the two terms of the
+    recurrence, 4 u (beta |x_prev| + (1 - beta) |y|) with u = 2^-24 (y = g or
+    g^2), which a fused multiply-add and a separate product and sum may
+    disagree by where the terms cancel;
+  * bf16 moments: the GPU's stored moment must be one of the bf16 roundings
+    of that float32 interval, i.e. it lies between the roundings of the
+    interval's ends.
+  * the weight delta is judged as above (W is computed from the unrounded
+    new moments on both sides); the epilogue consistency check needs the
+    GPU's unrounded moments and applies only with float32 state.
 """
 from __future__ import annotations
 
@@ -36,7 +53,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .ref import adamw_param
+from .floor import U32, StateFloor
+from .ref import adamw_param, adamw_step_mixed, bf16_round
 
 REL_STATE = 1e-4
 ABS_DW = 1e-3
@@ -147,3 +165,71 @@ def bitwise_equal(a, b) -> bool:
     a = np.ascontiguousarray(a, dtype=np.float32)
     b = np.ascontiguousarray(b, dtype=np.float32)
     return a.shape == b.shape and bool(np.array_equal(a.view(np.uint32), b.view(np.uint32)))
+
+
+def _f32_toward(x64, direction):
+    """Float32 values next to x64 on the given side (-1 below, +1 above)."""
+    x64 = np.asarray(x64, dtype=np.float64)
+    y = x64.astype(np.float32)
+    if direction < 0:
+        return np.where(y.astype(np.float64) > x64, np.nextafter(y, np.float32(-np.inf)), y)
+    return np.where(y.astype(np.float64) < x64, np.nextafter(y, np.float32(np.inf)), y)
+
+
+def bf16_bracket(lo64, hi64):
+    """Smallest and largest bf16 rounding of any float32 in [lo64, hi64]."""
+    return bf16_round(_f32_toward(lo64, -1)), bf16_round(_f32_toward(hi64, +1))
+
+
+def _check_bracket(name, x, lo, hi, checks):
+    x, lo, hi = _f64(x), _f64(lo), _f64(hi)
+    bad = ~((x >= lo) & (x <= hi))
+    checks[name] = {"fails": int(np.count_nonzero(bad)),
+                    "max_err": float(np.max(np.maximum(lo - x, x - hi))) if x.size else 0.0}
+    return not bad.any()
+
+
+def judge_adamw_mixed(step, W_prev, m_prev, v_prev, W_gpu, m_gpu, v_gpu, g_ref, tau,
+                      grad_bf16, state_bf16, lr, beta1, beta2, eps, weight_decay) -> Report:
+    """One AdamW step of a precision variant, both sides from (W_prev, m_prev,
+    v_prev); m, v arrays as float32 (bf16 values when state_bf16)."""
+    checks = {}
+    ok = True
+    g_ref = _f64(g_ref)
+    tau = _f64(tau)
+    if grad_bf16:
+        g_use = _f64(bf16_round(g_ref.astype(np.float32)))
+        g_lo, g_hi = bf16_bracket(g_ref - tau, g_ref + tau)
+        tau = np.maximum(_f64(g_hi) - g_use, g_use - _f64(g_lo))
+    else:
+        g_use = g_ref
+    W_ref, m32, v32 = adamw_step_mixed(W_prev, m_prev, v_prev, g_ref.astype(np.float32), step,
+                                       grad_bf16, False, lr, beta1, beta2, eps, weight_decay)
+    floor = StateFloor(np.shape(m32), "adamw", beta1, beta2)
+    floor.update(tau, g_use)
+    # float32 evaluation of beta x_prev + (1 - beta) y in any order (fused or
+    # not): at most a few roundings of the two terms, which matters where they
+    # cancel and the relative bar alone is too tight
+    arith_m = 4 * U32 * (beta1 * np.abs(_f64(m_prev)) + (1 - beta1) * np.abs(g_use))
+    arith_v = 4 * U32 * (beta2 * np.abs(_f64(v_prev)) + (1 - beta2) * g_use * g_use)
+    for name, x_gpu, x_ref, err in (("m", m_gpu, m32, floor.m_err + arith_m),
+                                    ("v", v_gpu, v32, floor.v_err + arith_v)):
+        allow = REL_STATE * np.abs(_f64(x_ref)) + err
+        if state_bf16:
+            lo, hi = bf16_bracket(_f64(x_ref) - allow, _f64(x_ref) + allow)
+            ok &= _check_bracket(name, x_gpu, lo, hi, checks)
+            checks[name + "_rounded_equal"] = float(np.mean(
+                _f64(x_gpu) == _f64(bf16_round(np.asarray(x_ref, np.float32)))))
+        else:
+            ok &= _check(name, np.abs(_f64(x_gpu) - _f64(x_ref)), allow, checks)
+    d_gpu = _f64(W_gpu) - _f64(W_prev)
+    d_ref = _f64(W_ref) - _f64(W_prev)
+    D = update_floor(step, m32, v32, floor, beta1, beta2, eps, zero_start=False)
+    checks["ambiguous"] = int(np.count_nonzero(D > ABS_DW))
+    ok &= _check("dW", np.abs(d_gpu - d_ref), ABS_DW * lr + lr * D, checks)
+    if not state_bf16:
+        W_cons = adamw_param(W_prev, m_gpu, v_gpu, step, lr, beta1, beta2, eps, weight_decay)
+        ok &= _check("epilogue", np.abs(_f64(W_gpu) - _f64(W_cons)),
+                     np.full(d_gpu.shape, ABS_DW * lr), checks)
+    checks["normwise_dW"] = normwise(d_gpu, d_ref)
+    return Report(bool(ok), checks)

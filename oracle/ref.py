@@ -145,6 +145,64 @@ def adamw_step(W, m, v, g, step: int, lr: float = 1e-3, beta1: float = 0.9,
 
 
 # --------------------------------------------------------------------------
+# Precision variants (FORGE assessment, "What's already in tree and easy to
+# miss": the existing lowering truncates the float32 accumulator to bf16;
+# "Math verified, not asserted", P6: float32 vs bf16 gradient and state)
+# --------------------------------------------------------------------------
+def bf16_round(x) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to even), as float32.
+
+    bf16 keeps the top 16 bits of the float32 pattern; rounding adds half of
+    the dropped part, plus one if the kept part is odd, before truncating.
+    The exponent range is float32's, so the same bit arithmetic rounds
+    subnormals and overflows to infinity correctly. NaN stays NaN (quiet).
+    """
+    a = np.ascontiguousarray(np.asarray(x, dtype=F32))
+    u = a.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = r.astype(np.uint32).view(F32).copy()
+    nan = np.isnan(a)
+    out[nan] = a[nan]
+    return out
+
+
+def adamw_step_mixed(W, m, v, g, step: int, grad_bf16: bool, state_bf16: bool,
+                     lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.01):
+    """One AdamW step with a bf16-rounded gradient and/or bf16 moments.
+
+    grad_bf16: the gradient is rounded to bf16 before the step (the unfused
+    path that stores a bf16 gradient). state_bf16: m, v hold bf16 values; the
+    step computes the new float32 moments, updates W from them, and stores
+    them rounded to bf16. Otherwise the float32 step of adamw_step.
+    """
+    g = bf16_round(g) if grad_bf16 else np.asarray(g, dtype=F32)
+    m_new, v_new = adamw_moments(m, v, g, beta1, beta2)
+    W_new = adamw_param(W, m_new, v_new, step, lr, beta1, beta2, eps, weight_decay)
+    if state_bf16:
+        m_new, v_new = bf16_round(m_new), bf16_round(v_new)
+    return W_new, m_new, v_new
+
+
+def wgrad_f64(X_bits: np.ndarray, dY_bits: np.ndarray) -> np.ndarray:
+    """The weight gradient in float64, not rounded (precision reference)."""
+    return bf16_bits_to_f64(dY_bits).T @ bf16_bits_to_f64(X_bits)
+
+
+def adamw_step_f64(W, m, v, g, step: int, lr: float = 1e-3, beta1: float = 0.9,
+                   beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01):
+    """AdamW in float64 throughout (the reference the precision variants are
+    measured against); same formula as adamw_step."""
+    W = np.asarray(W, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** step)
+    v_hat = v / (1.0 - beta2 ** step)
+    return W - lr * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * W), m, v
+
+
+# --------------------------------------------------------------------------
 # SGD with momentum, float32
 # --------------------------------------------------------------------------
 def sgdm_step(W, b, g, lr: float = 1e-3, momentum: float = 0.9, weight_decay: float = 0.0,
