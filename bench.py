@@ -7,7 +7,9 @@ resident in HBM: dW = X^T dY (bf16 in, fp32 accumulate, all tokens) consumed by
 AdamW in the epilogue, W/m/v updated in place. The default workload is a
 Llama-3-8B MLP down projection (X [8192, 14336], dY [8192, 4096], fp32 W/m/v
 [4096, 14336]). The unfused pair (fp32 gradient stored, then elementwise AdamW)
-is timed beside it, and the CPU oracle on a bounded sample.
+is timed beside it, then (dense AdamW workloads) two precision variants: fused
+AdamW with bf16 moments, and the bf16-rounded gradient stored and followed by
+elementwise AdamW; and the CPU oracle on a bounded sample.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -83,6 +85,8 @@ def main():
     ap.add_argument("--pool", type=int, default=2, help="distinct input batches cycled")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the precision-variant legs (dense AdamW workloads)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -203,6 +207,37 @@ def main():
         log(f"[bench] unfused: {u_step:.4f} ms/step")
         del grad
 
+    variants = None
+    if not args.no_variants and opt == "adamw" and not grouped:
+        # Precision variants on the same workload: fused AdamW with bf16 moments,
+        # and the lowering the fusion replaces (gradient rounded to bf16 and
+        # stored, then elementwise AdamW on float32 state).
+        mb = torch.zeros(W.shape, device=dev, dtype=torch.bfloat16)
+        vb = torch.zeros_like(mb)
+        gb = torch.empty(W.shape, device=dev, dtype=torch.bfloat16)
+
+        def fused_bf16_state(step, batch):
+            X, dY, _, _ = batch
+            wg.forge_wgrad_adamw_bf16state(X, dY, W, mb, vb, step=step, tile=args.tile, **hp)
+
+        def bf16_grad_unfused(step, batch):
+            X, dY, _, _ = batch
+            wg.forge_wgrad_bf16(X, dY, gb, tile=args.tile)
+            wg.forge_adamw_mixed(gb, W, m, v, step=step, **hp)
+
+        variants = {}
+        for name, fn, nbytes in (("fused_adamw_bf16_state", fused_bf16_state,
+                                  x_bytes + 16 * n_param),
+                                 ("bf16_gradient_then_adamw", bf16_grad_unfused,
+                                  x_bytes + 28 * n_param)):
+            v_step, v_kernel, _ = timed(fn, args.steps, args.warmup)
+            variants[name] = {"ms_per_step": round(v_step, 5),
+                              "tflops": round(flops / v_step / 1e9, 2),
+                              "alg_hbm_bytes": nbytes,
+                              "frac_bf16_peak": round(flops / v_step / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            log(f"[bench] {name}: {v_step:.4f} ms/step")
+        del mb, vb, gb
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         a = torch.ones(n, device=dev)
@@ -300,6 +335,7 @@ def main():
         "alg_hbm_gbs": round(alg_bytes / ms_kernel / 1e6, 1),
         "hbm_frac_alg": round(alg_bytes / ms_kernel / 1e6 / PEAK_HBM_GBS, 4),
         "unfused": unfused,
+        "precision_variants": variants,
         "kernel_source_sha": sha,
         "cpu_baseline": cpu,
     }

@@ -82,8 +82,13 @@ enum {
   FORGE_ERR_CLIP_NOT_FUSABLE = 6, /* a global-norm clip was requested                    */
   FORGE_ERR_TILE = 7,             /* unknown tile id                                     */
   FORGE_ERR_DEVICE = 8,           /* current device is not gfx950, or no device          */
-  FORGE_ERR_LAUNCH = 9            /* the HIP runtime rejected the launch                 */
+  FORGE_ERR_LAUNCH = 9,           /* the HIP runtime rejected the launch                 */
+  FORGE_ERR_DTYPE = 10            /* unknown element type                                */
 };
+
+/* Element types of the precision-variant calls. bf16 is raw 16-bit storage. */
+typedef int32_t forge_dtype;
+enum { FORGE_F32 = 0, FORGE_BF16 = 1 };
 
 /*
  * AdamW with decoupled weight decay, float32 state. For step t (1-based):
@@ -210,6 +215,45 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
                                        float* W, float* m, float* v,
                                        int64_t d_in, int64_t d_out,
                                        const forge_adamw_params* p, forge_tile tile, void* stream);
+
+/*
+ * Precision variants. FORGE assessment, "What's already in tree and easy to
+ * miss": the existing lowering accumulates a bf16 matmul in float32 and then
+ * truncates to bf16, and that truncation is exactly the rounding the fused
+ * path deletes; "Math verified, not asserted", P6: the float32-accumulator
+ * benefit is worth ~900x with float32 optimizer state and ~1x with bf16
+ * state. These calls make every combination measurable on the GPU.
+ *
+ * forge_wgrad_bf16: the unfused gradient, rounded to bf16 (nearest even)
+ *   from the same float32 accumulator forge_wgrad stores; grad_bf16 is
+ *   [d_out, d_in] 16-bit storage, 16-byte aligned.
+ */
+FORGE_API forge_status forge_wgrad_bf16(const void* X, const void* dY, void* grad_bf16,
+                              int64_t T, int64_t d_in, int64_t d_out, forge_tile tile,
+                              void* stream);
+
+/*
+ * Fused weight gradient + AdamW with bf16 optimizer state: m, v are [d_out,
+ * d_in] bf16 storage, W float32. Each step decodes m, v to float32, runs the
+ * same float32 arithmetic as forge_wgrad_adamw (W is updated from the
+ * unrounded new moments) and stores m, v rounded to bf16 (nearest even).
+ * Contract otherwise as forge_wgrad_adamw.
+ */
+FORGE_API forge_status forge_wgrad_adamw_bf16state(const void* X, const void* dY, float* W,
+                                         void* m_bf16, void* v_bf16, int64_t T, int64_t d_in,
+                                         int64_t d_out, const forge_adamw_params* p,
+                                         forge_tile tile, void* stream);
+
+/*
+ * Elementwise AdamW with the gradient and the state (m, v) each float32 or
+ * bf16 (W float32): the unfused pair for every precision combination. The
+ * arithmetic is forge_adamw's; bf16 state is decoded before and rounded
+ * (nearest even) after the step. Unknown types return FORGE_ERR_DTYPE.
+ * Contract otherwise as forge_adamw.
+ */
+FORGE_API forge_status forge_adamw_mixed(const void* grad, forge_dtype grad_dtype, float* W,
+                               void* m, void* v, forge_dtype state_dtype, int64_t n,
+                               const forge_adamw_params* p, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 FORGE_API const char* forge_status_string(forge_status s);

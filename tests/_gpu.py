@@ -39,6 +39,15 @@ def host(t, rows=None) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def host_f32(t, rows=None) -> np.ndarray:
+    """As host(), for float32 or bfloat16 tensors (bf16 widened exactly)."""
+    torch = torch_mod()
+    if rows is not None:
+        idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+        t = t.index_select(t.dim() - 2, idx)
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
 def sample_rows(d_out: int, bn: int = 128, per_tile: int = 2, extra: int = 16, seed: int = 0):
     """Rows of W spread over every 128-row block (first/last of each block,
     plus random ones)."""

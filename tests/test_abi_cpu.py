@@ -34,9 +34,10 @@ def declared_symbols(root):
 
 def test_every_declared_symbol_is_exported(lib, root):
     names = declared_symbols(root)
-    assert names == sorted(["forge_adamw", "forge_grouped_wgrad_adamw", "forge_sgdm",
-                            "forge_status_string", "forge_wgrad", "forge_wgrad_adamw",
-                            "forge_wgrad_sgdm"])
+    assert names == sorted(["forge_adamw", "forge_adamw_mixed", "forge_grouped_wgrad_adamw",
+                            "forge_sgdm", "forge_status_string", "forge_wgrad",
+                            "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
+                            "forge_wgrad_bf16", "forge_wgrad_sgdm"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path], check=True,
@@ -46,10 +47,11 @@ def test_every_declared_symbol_is_exported(lib, root):
 
 
 def test_status_strings(lib):
-    for s in range(-1, 11):
+    for s in range(-1, 12):
         txt = _lib.forge_status_string(s)
         assert isinstance(txt, str) and txt
     assert "clipping" in _lib.forge_status_string(6)
+    assert "element type" in _lib.forge_status_string(10)
 
 
 def adam(**kw):
@@ -116,6 +118,10 @@ def test_no_gpu_means_device_error(lib):
     offs = (ctypes.c_int64 * 3)(0, 10, 10)
     assert lib.forge_grouped_wgrad_adamw(X_ADDR, Y_ADDR, offs, 2, A, B, C, 64, 32,
                                          ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, A, 64, 64, 32, 0, None) == 8
+    assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, C, 64, 64, 32,
+                                           ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_adamw_mixed(A, 1, B, C, D, 1, 100, ctypes.byref(adam()), None) == 8
 
 
 def test_sgdm_and_unfused_reject(lib):
@@ -132,6 +138,35 @@ def test_sgdm_and_unfused_reject(lib):
     assert lib.forge_adamw(A + 4, B, C, D, 100, ctypes.byref(adam()), None) == 3
     assert lib.forge_adamw(A, B, C, D, 100, None, None) == 1
     assert lib.forge_sgdm(A, B, NULL, 100, ctypes.byref(sgd()), None) == 1
+
+
+def test_precision_variants_reject(lib):
+    F32, BF16 = _lib.FORGE_F32, _lib.FORGE_BF16
+    n = 128
+    # bf16 buffers are 2 bytes per element: m at A + 2n does not overlap a bf16 grad at A
+    assert lib.forge_adamw_mixed(A, BF16, B, A + 2 * n, C, BF16, n, ctypes.byref(adam()),
+                                 None) != 4
+    # ... but does overlap a float32 grad at A
+    assert lib.forge_adamw_mixed(A, F32, B, A + 2 * n, C, BF16, n, ctypes.byref(adam()),
+                                 None) == 4
+    assert lib.forge_adamw_mixed(A, 7, B, C, D, F32, n, ctypes.byref(adam()), None) == 10
+    assert lib.forge_adamw_mixed(A, F32, B, C, D, -1, n, ctypes.byref(adam()), None) == 10
+    assert lib.forge_adamw_mixed(A, BF16, B, C, D, BF16, n, ctypes.byref(adam(max_grad_norm=1.0)),
+                                 None) == 6
+    assert lib.forge_adamw_mixed(A, BF16, B, C + 8, D, BF16, n, ctypes.byref(adam()), None) == 3
+    # bf16 gradient: [32, 64] bf16 is 4 KiB, so an X 4 KiB after it does not overlap
+    assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, X_ADDR - 4096, 64, 64, 32, 0, None) != 4
+    assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, X_ADDR - 2048, 64, 64, 32, 0, None) == 4
+    assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, NULL, 64, 64, 32, 0, None) == 1
+    assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, A, 64, 64, 32, 9, None) == 7
+    p = adam()
+    assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, B + 2 * 64 * 32, 64, 64, 32,
+                                           ctypes.byref(p), 0, None) != 4
+    assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, B + 2 * 64 * 32 - 16, 64, 64,
+                                           32, ctypes.byref(p), 0, None) == 4
+    p = adam(max_grad_norm=3.0)
+    assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, C, 64, 64, 32, ctypes.byref(p),
+                                           0, None) == 6
 
 
 def test_grouped_rejects(lib):

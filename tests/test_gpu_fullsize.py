@@ -9,8 +9,9 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, f32_dev, host, log, run_dense_adamw,
-                        run_dense_sgdm, sample_rows, torch_mod)
+from oracle import judge
+from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, f32_dev, host, host_f32, log,
+                        run_dense_adamw, run_dense_sgdm, sample_rows, torch_mod)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -29,6 +30,39 @@ def test_mlp_down_adamw_10_steps(wg):
     """Llama-3-8B MLP down projection: T=8192, d_in=14336, d_out=4096."""
     case = synth.dense_case(1)
     run_dense_adamw(wg, case, case.steps, tile=0, rows=sample_rows(case.d_out))
+
+
+def test_mlp_down_bf16_state_and_bf16_gradient(wg):
+    """The precision variants at the MLP-down size: fused AdamW with bf16
+    moments for 3 steps, and the bf16-rounded gradient (FORGE assessment, P6)."""
+    torch = torch_mod()
+    case = synth.dense_case(1)
+    rows = sample_rows(case.d_out)
+    hp = adamw_hp(case)
+    W0, _, _ = synth.dense_state(case)
+    W = f32_dev(W0)
+    m = torch.zeros(W.shape, device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros_like(m)
+    for t in range(1, 4):
+        Xb, dYb = synth.dense_inputs(case, t)
+        log(f"[{case.name}] bf16 state step {t}")
+        W_prev, m_prev, v_prev = host(W, rows), host_f32(m, rows), host_f32(v, rows)
+        wg.forge_wgrad_adamw_bf16state(bf16_dev(Xb), bf16_dev(dYb), W, m, v, step=t, **hp)
+        torch.cuda.synchronize()
+        rep = judge.judge_adamw_mixed(t, W_prev, m_prev, v_prev, host(W, rows), host_f32(m, rows),
+                                      host_f32(v, rows), oracle.wgrad_rows(Xb, dYb, rows),
+                                      oracle.acc_floor_rows(Xb, dYb, rows), False, True, **hp)
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+    log(f"[{case.name}] bf16 gradient")
+    g = torch.empty(W.shape, device="cuda", dtype=torch.bfloat16)
+    wg.forge_wgrad_bf16(bf16_dev(Xb), bf16_dev(dYb), g)
+    torch.cuda.synchronize()
+    g_ref = oracle.wgrad_rows(Xb, dYb, rows)
+    tau = oracle.acc_floor_rows(Xb, dYb, rows)
+    lo, hi = judge.bf16_bracket(g_ref - tau, g_ref + tau)
+    got = host_f32(g, rows)
+    assert np.all((got >= lo) & (got <= hi))
 
 
 def test_qkv_adamw_and_sgdm(wg):

@@ -1,0 +1,221 @@
+"""GPU parity of the precision variants (page "docs(audit): FORGE assessment +
+residency-aware epilogue-fusion track", sections "What's already in tree and
+easy to miss" and "Math verified, not asserted", P6):
+
+  forge_wgrad_bf16              gradient rounded once to bf16 (the lowering the
+                                fusion removes; the baseline of P6)
+  forge_adamw_mixed             elementwise AdamW, bf16 or float32 gradient and state
+  forge_wgrad_adamw_bf16state   fused AdamW with bf16 moments
+
+Accuracy against the oracle, each step judged from the GPU's previous state
+(oracle.judge.judge_adamw_mixed); bitwise invariance between the fused and
+unfused bf16-state routes; and the P6 study on the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import judge, precision_study
+from synth import DenseCase
+from tests._gpu import (adamw_hp, bf16_dev, bits_equal, f32_dev, host, host_f32, log,
+                        torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wg():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_gradient_gemm_amd as wg
+    wg.library()
+    return wg
+
+
+def _sync():
+    torch_mod().cuda.synchronize()
+
+
+def _bf16_state(a: np.ndarray):
+    """Device bf16 tensor holding a (whose values must be bf16 values)."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    out = t.to(torch.bfloat16)
+    assert bits_equal(out.to(torch.float32).cpu().numpy(), a)
+    return out
+
+
+RAGGED = DenseCase("ragged_77x264x200", T=77, d_in=264, d_out=200, seed_base=57000, steps=3)
+MANY = DenseCase("tiles_300x520x392", T=300, d_in=520, d_out=392, seed_base=58000, steps=2)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("case", [RAGGED, MANY], ids=lambda c: c.name)
+def test_wgrad_bf16_against_oracle(wg, case, tile):
+    torch = torch_mod()
+    Xb, dYb = synth.dense_inputs(case, 1)
+    log(f"[{case.name}] wgrad_bf16 tile {tile}")
+    g = torch.full((case.d_out, case.d_in), float("nan"), device="cuda").to(torch.bfloat16)
+    wg.forge_wgrad_bf16(bf16_dev(Xb), bf16_dev(dYb), g, tile=tile)
+    _sync()
+    got = host_f32(g)
+    g_ref = oracle.wgrad(Xb, dYb)
+    tau = oracle.acc_floor(Xb, dYb)
+    lo, hi = judge.bf16_bracket(g_ref - tau, g_ref + tau)
+    assert np.all((got >= lo) & (got <= hi))
+    log(f"  equal to the oracle's rounding: "
+        f"{np.mean(got == oracle.bf16_round(g_ref.astype(np.float32))):.6f}")
+    # invariance: the bf16 output is the float32 accumulator rounded once
+    g32 = torch.empty((case.d_out, case.d_in), device="cuda")
+    wg.forge_wgrad(bf16_dev(Xb), bf16_dev(dYb), g32, tile=tile)
+    _sync()
+    assert bits_equal(host_f32(g32.to(torch.bfloat16)), got)
+
+
+@pytest.mark.parametrize("grad_bf16,state_bf16", [(False, False), (True, False), (False, True),
+                                                  (True, True)])
+def test_adamw_mixed_elementwise(wg, grad_bf16, state_bf16):
+    torch = torch_mod()
+    n = 3 * 4096 + 5                                 # several blocks and a ragged tail
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W = synth.normal_f32(300, (n,), 0.02)
+    m = synth.normal_f32(301, (n,), 1e-2)
+    v = np.abs(synth.normal_f32(302, (n,), 1e-4))
+    if state_bf16:
+        m, v = oracle.bf16_round(m), oracle.bf16_round(v)
+    Wd = f32_dev(W)
+    md, vd = (_bf16_state(m), _bf16_state(v)) if state_bf16 else (f32_dev(m), f32_dev(v))
+    for t in (1, 2, 3):
+        g = synth.normal_f32(310 + t, (n,))
+        if grad_bf16:
+            g = oracle.bf16_round(g)
+            gd = _bf16_state(g)
+        else:
+            gd = f32_dev(g)
+        log(f"[adamw_mixed n={n} grad_bf16={grad_bf16} state_bf16={state_bf16}] step {t}")
+        W_prev, m_prev, v_prev = W, m, v
+        wg.forge_adamw_mixed(gd, Wd, md, vd, step=t + 4, **hp)
+        _sync()
+        W, m, v = host(Wd), host_f32(md), host_f32(vd)
+        rep = judge.judge_adamw_mixed(t + 4, W_prev, m_prev, v_prev, W, m, v, g,
+                                      np.zeros(n), grad_bf16, state_bf16, **hp)
+        log(f"  {rep}")
+        assert rep.passed, str(rep)
+
+
+def _run_variant_dense(wg, case, tile, grad_bf16, state_bf16, steps, fused=True):
+    """AdamW steps of a precision variant; each judged from the GPU's previous
+    state. Returns the final device (W, m, v)."""
+    torch = torch_mod()
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W = f32_dev(W0)
+    if state_bf16:
+        m0, v0 = oracle.bf16_round(m0), oracle.bf16_round(v0)
+        m, v = _bf16_state(m0), _bf16_state(v0)
+    else:
+        m, v = f32_dev(m0), f32_dev(v0)
+    for t in range(1, steps + 1):
+        Xb, dYb = synth.dense_inputs(case, t)
+        X, dY = bf16_dev(Xb), bf16_dev(dYb)
+        log(f"[{case.name}] grad_bf16={grad_bf16} state_bf16={state_bf16} fused={fused} "
+            f"tile {tile} step {t}")
+        W_prev, m_prev, v_prev = host(W), host_f32(m), host_f32(v)
+        if grad_bf16:
+            g = torch.empty((case.d_out, case.d_in), device="cuda").to(torch.bfloat16)
+            wg.forge_wgrad_bf16(X, dY, g, tile=tile)
+            wg.forge_adamw_mixed(g, W, m, v, step=t, **hp)
+        elif state_bf16 and fused:
+            wg.forge_wgrad_adamw_bf16state(X, dY, W, m, v, step=t, tile=tile, **hp)
+        else:
+            g = torch.empty((case.d_out, case.d_in), device="cuda")
+            wg.forge_wgrad(X, dY, g, tile=tile)
+            wg.forge_adamw_mixed(g, W, m, v, step=t, **hp)
+        _sync()
+        rep = judge.judge_adamw_mixed(t, W_prev, m_prev, v_prev, host(W), host_f32(m), host_f32(v),
+                                      oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb),
+                                      grad_bf16, state_bf16, **hp)
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+    return W, m, v
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_fused_bf16_state(wg, tile):
+    _run_variant_dense(wg, RAGGED, tile, False, True, RAGGED.steps)
+
+
+def test_fused_bf16_state_many_tiles(wg):
+    _run_variant_dense(wg, MANY, 0, False, True, MANY.steps)
+
+
+@pytest.mark.parametrize("state_bf16", [False, True])
+def test_bf16_gradient_then_adamw(wg, state_bf16):
+    _run_variant_dense(wg, RAGGED, 1, True, state_bf16, RAGGED.steps)
+
+
+def test_fused_bf16_state_equals_unfused(wg):
+    """Fused bf16-state AdamW is bitwise the stored float32 gradient followed
+    by the elementwise bf16-state step (FORGE assessment, P1), on every tiling."""
+    base = _run_variant_dense(wg, MANY, 1, False, True, 2, fused=False)
+    base = [host_f32(x) for x in base]
+    for tile in (1, 2, 3, 4):
+        out = [host_f32(x) for x in _run_variant_dense(wg, MANY, tile, False, True, 2)]
+        assert all(bits_equal(a, b) for a, b in zip(out, base)), tile
+
+
+def test_zero_tokens_bf16_state_decays(wg):
+    torch = torch_mod()
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(320, (32, 64), 0.02)
+    m0 = oracle.bf16_round(synth.normal_f32(321, W0.shape, 0.1))
+    v0 = oracle.bf16_round(np.abs(synth.normal_f32(322, W0.shape, 0.01)))
+    W, m, v = f32_dev(W0), _bf16_state(m0), _bf16_state(v0)
+    wg.forge_wgrad_adamw_bf16state(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+                                   torch.empty((0, 32), dtype=torch.bfloat16, device="cuda"),
+                                   W, m, v, step=3, **hp)
+    _sync()
+    rep = judge.judge_adamw_mixed(3, W0, m0, v0, host(W), host_f32(m), host_f32(v),
+                                  np.zeros_like(W0), np.zeros(W0.shape), False, True, **hp)
+    assert rep.passed, str(rep)
+
+
+def test_p6_precision_study_on_gpu(wg):
+    """P6 on the GPU: the float32 gradient against the bf16-rounded one, with
+    float32 and with bf16 moments, each run against the oracle's float64 run."""
+    torch = torch_mod()
+    d_in = d_out = 512
+    T, steps, seed = 4096, 8, 21
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(seed, (d_out, d_in), 0.02)
+    inputs = [(synth.normal_bf16(seed + 2 * t, (T, d_in)),
+               synth.normal_bf16(seed + 2 * t + 1, (T, d_out))) for t in range(1, steps + 1)]
+    runs = {}
+    for name, (gb, sb) in precision_study.VARIANTS.items():
+        log(f"[p6] {name}")
+        W = f32_dev(W0)
+        sdt = torch.bfloat16 if sb else torch.float32
+        m = torch.zeros((d_out, d_in), device="cuda", dtype=sdt)
+        v = torch.zeros((d_out, d_in), device="cuda", dtype=sdt)
+        for t, (Xb, dYb) in enumerate(inputs, start=1):
+            X, dY = bf16_dev(Xb), bf16_dev(dYb)
+            if gb:
+                g = torch.empty((d_out, d_in), device="cuda", dtype=torch.bfloat16)
+                wg.forge_wgrad_bf16(X, dY, g)
+                wg.forge_adamw_mixed(g, W, m, v, step=t, **hp)
+            elif sb:
+                wg.forge_wgrad_adamw_bf16state(X, dY, W, m, v, step=t, **hp)
+            else:
+                wg.forge_wgrad_adamw(X, dY, W, m, v, step=t, **hp)
+        _sync()
+        runs[name] = (host(W), host_f32(m), host_f32(v))
+    ref = precision_study.reference_run(W0, inputs, hp)
+    err = precision_study.errors(W0, runs, ref)
+    ben = precision_study.benefits(err)
+    for name, e in err.items():
+        log(f"  {name:11s} dW {e['dW']:.3e}  m {e['m']:.3e}  v {e['v']:.3e}")
+    log(f"  benefit fp32 state {ben['fp32_state']}  bf16 state {ben['bf16_state']}")
+    assert ben["fp32_state"]["dW"] > 100, ben
+    assert 0.7 < ben["bf16_state"]["dW"] < 2.0, ben

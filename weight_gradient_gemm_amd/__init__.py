@@ -12,14 +12,19 @@ from ._lib import (  # noqa: F401
     FORGE_TILE_256x256,
     FORGE_TILE_PERSISTENT,
     FORGE_TILE_DEFAULT,
+    FORGE_BF16,
+    FORGE_F32,
     ForgeError,
     STATUS,
     forge_adamw,
+    forge_adamw_mixed,
     forge_grouped_wgrad_adamw,
     forge_sgdm,
     forge_status_string,
     forge_wgrad,
     forge_wgrad_adamw,
+    forge_wgrad_adamw_bf16state,
+    forge_wgrad_bf16,
     forge_wgrad_sgdm,
     library,
     library_path,

@@ -19,10 +19,13 @@ FORGE_TILE_128x128 = 2
 FORGE_TILE_256x256 = 3
 FORGE_TILE_PERSISTENT = 4
 
+FORGE_F32 = 0
+FORGE_BF16 = 1
+
 STATUS = {
     0: "FORGE_OK", 1: "FORGE_ERR_NULL", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_ALIGN",
     4: "FORGE_ERR_ALIAS", 5: "FORGE_ERR_HPARAM", 6: "FORGE_ERR_CLIP_NOT_FUSABLE",
-    7: "FORGE_ERR_TILE", 8: "FORGE_ERR_DEVICE", 9: "FORGE_ERR_LAUNCH",
+    7: "FORGE_ERR_TILE", 8: "FORGE_ERR_DEVICE", 9: "FORGE_ERR_LAUNCH", 10: "FORGE_ERR_DTYPE",
 }
 
 _i64 = ctypes.c_int64
@@ -69,10 +72,16 @@ def library() -> ctypes.CDLL:
         lib.forge_grouped_wgrad_adamw.argtypes = [_vp, _vp, ctypes.POINTER(_i64), _i32, _vp, _vp,
                                                   _vp, _i64, _i64, ctypes.POINTER(AdamWParams),
                                                   _i32, _vp]
+        lib.forge_wgrad_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
+        lib.forge_wgrad_adamw_bf16state.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                                    ctypes.POINTER(AdamWParams), _i32, _vp]
+        lib.forge_adamw_mixed.argtypes = [_vp, _i32, _vp, _vp, _vp, _i32, _i64,
+                                          ctypes.POINTER(AdamWParams), _vp]
         lib.forge_status_string.argtypes = [_i32]
         lib.forge_status_string.restype = ctypes.c_char_p
         for name in ("forge_wgrad_adamw", "forge_wgrad_sgdm", "forge_wgrad", "forge_adamw",
-                     "forge_sgdm", "forge_grouped_wgrad_adamw"):
+                     "forge_sgdm", "forge_grouped_wgrad_adamw", "forge_wgrad_bf16",
+                     "forge_wgrad_adamw_bf16state", "forge_adamw_mixed"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -133,12 +142,33 @@ def _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm):
                        int(step), float(max_grad_norm))
 
 
-def _state_like(W, others, d_out, d_in, lead=()):
+def _state_like(W, others, d_out, d_in, lead=(), dtype=None):
+    """Shape (and dtype: float32 unless given) of W and the state tensors."""
     want = (*lead, d_out, d_in)
     for name, t in (("W", W), *others):
         if tuple(t.shape) != want:
             raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
-        _want(t, _torch().float32, name)
+        _want(t, (dtype or {}).get(name, _torch().float32), name)
+
+
+def _xdy(X, dY):
+    torch = _torch()
+    _want(X, torch.bfloat16, "X")
+    _want(dY, torch.bfloat16, "dY")
+    T, d_in = _shape2(X, "X")
+    T2, d_out = _shape2(dY, "dY")
+    if T2 != T:
+        raise ValueError(f"X has {T} token rows, dY has {T2}")
+    return T, d_in, d_out
+
+
+def _dtype_code(t, name):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FORGE_F32
+    if t.dtype == torch.bfloat16:
+        return FORGE_BF16
+    raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
 
 
 # --------------------------------------------------------------------------
@@ -246,3 +276,50 @@ def forge_grouped_wgrad_adamw(X_perm, dY_perm, offsets, W, m, v, *, step, lr=1e-
                                                _ptr(m), _ptr(v), d_in, d_out, ctypes.byref(p),
                                                int(tile), _stream(stream)),
            "forge_grouped_wgrad_adamw")
+
+
+# --------------------------------------------------------------------------
+# precision variants
+# --------------------------------------------------------------------------
+def forge_wgrad_bf16(X, dY, grad, *, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """grad (bfloat16) <- dY^T X rounded to bf16 from the float32 accumulator."""
+    torch = _torch()
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(grad, (), d_out, d_in, dtype={"W": torch.bfloat16})
+    _check(library().forge_wgrad_bf16(_ptr(X), _ptr(dY), _ptr(grad), T, d_in, d_out, int(tile),
+                                      _stream(stream)), "forge_wgrad_bf16")
+
+
+def forge_wgrad_adamw_bf16state(X, dY, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                                tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """Fused AdamW with m, v in bfloat16 (W float32), in place."""
+    torch = _torch()
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in,
+                dtype={"m": torch.bfloat16, "v": torch.bfloat16})
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_wgrad_adamw_bf16state(_ptr(X), _ptr(dY), _ptr(W), _ptr(m), _ptr(v), T,
+                                                 d_in, d_out, ctypes.byref(p), int(tile),
+                                                 _stream(stream)),
+           "forge_wgrad_adamw_bf16state")
+
+
+def forge_adamw_mixed(grad, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                      weight_decay=0.01, max_grad_norm=0.0, stream=None) -> None:
+    """Elementwise AdamW; grad and the state (m, v, one dtype) float32 or bfloat16."""
+    torch = _torch()
+    _want(W, torch.float32, "W")
+    gd = _dtype_code(grad, "grad")
+    sd = _dtype_code(m, "m")
+    if v.dtype != m.dtype:
+        raise TypeError(f"m and v must share a dtype, got {m.dtype} and {v.dtype}")
+    for name, t in (("grad", grad), ("m", m), ("v", v)):
+        _want(t, t.dtype, name)
+    for name, t in (("W", W), ("m", m), ("v", v)):
+        if t.numel() != grad.numel():
+            raise ValueError(f"{name} has {t.numel()} elements, grad has {grad.numel()}")
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_adamw_mixed(_ptr(grad), gd, _ptr(W), _ptr(m), _ptr(v), sd,
+                                       grad.numel(), ctypes.byref(p), _stream(stream)),
+           "forge_adamw_mixed")

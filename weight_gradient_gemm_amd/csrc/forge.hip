@@ -194,9 +194,9 @@ forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
 }
 
 // AdamW epilogue variant: the exact square root when eps = 0.
-template <template <int> class F, class... Args>
+template <template <int> class F, int BASE = EPI_ADAMW, class... Args>
 forge_status with_adamw_epi(const forge_adamw_params& p, Args&&... args) {
-  return p.eps > 0.0 ? F<EPI_ADAMW>::run(args...) : F<EPI_ADAMW_EXACT>::run(args...);
+  return p.eps > 0.0 ? F<BASE>::run(args...) : F<BASE | EPI_EXACT_SQRT>::run(args...);
 }
 
 template <int EPI>
@@ -227,15 +227,26 @@ struct GroupedLaunch {
   }
 };
 
+template <bool EXACT, bool GRAD_BF16, bool STATE_BF16>
+forge_status launch_adamw_elementwise(const void* grad, float* W, void* m, void* v, int64_t n,
+                                      const AdamWConsts& c, hipStream_t s) {
+  const int64_t n4 = (n + 3) / 4;
+  const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
+  hipLaunchKernelGGL((adamw_elementwise_kernel<EXACT, GRAD_BF16, STATE_BF16>), dim3(blocks),
+                     dim3(256), 0, s, grad, W, m, v, n, c);
+  return launch_status();
+}
+
 template <int EPI>
 struct ElementwiseAdamW {
-  static forge_status run(const float* grad, float* W, float* m, float* v, int64_t n,
-                          const AdamWConsts& c, hipStream_t s) {
-    const int64_t n4 = (n + 3) / 4;
-    const int blocks = int(std::min<int64_t>((n4 + 255) / 256, 256 * 16));
-    hipLaunchKernelGGL(adamw_elementwise_kernel<EPI == EPI_ADAMW_EXACT>, dim3(blocks), dim3(256),
-                       0, s, grad, W, m, v, n, c);
-    return launch_status();
+  static forge_status run(const void* grad, bool grad_bf16, float* W, void* m, void* v,
+                          bool state_bf16, int64_t n, const AdamWConsts& c, hipStream_t s) {
+    constexpr bool X = (EPI & EPI_EXACT_SQRT) != 0;
+    if (grad_bf16)
+      return state_bf16 ? launch_adamw_elementwise<X, true, true>(grad, W, m, v, n, c, s)
+                        : launch_adamw_elementwise<X, true, false>(grad, W, m, v, n, c, s);
+    return state_bf16 ? launch_adamw_elementwise<X, false, true>(grad, W, m, v, n, c, s)
+                      : launch_adamw_elementwise<X, false, false>(grad, W, m, v, n, c, s);
   }
 };
 
@@ -314,7 +325,7 @@ FORGE_API forge_status forge_adamw(const float* grad, float* W, float* m, float*
   if (n == 0) return FORGE_OK;
   if (forge_status s = check_device()) return s;
   (void)hipGetLastError();
-  return with_adamw_epi<ElementwiseAdamW>(*p, grad, W, m, v, n, make_adamw(*p),
+  return with_adamw_epi<ElementwiseAdamW>(*p, grad, false, W, m, v, false, n, make_adamw(*p),
                                           static_cast<hipStream_t>(stream));
 }
 
@@ -358,6 +369,52 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
   return with_adamw_epi<GroupedLaunch>(*p, a, gt, E, tile, static_cast<hipStream_t>(stream));
 }
 
+FORGE_API forge_status forge_wgrad_bf16(const void* X, const void* dY, void* grad_bf16,
+                                        int64_t T, int64_t d_in, int64_t d_out, forge_tile tile,
+                                        void* stream) {
+  if (forge_status s = validate_wgrad_bf16(X, dY, grad_bf16, T, d_in, d_out, tile)) return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, static_cast<float*>(grad_bf16), nullptr, nullptr, T, d_in, d_out);
+  return launch_dense<EPI_GRAD | EPI_BF16_OUT>(a, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_wgrad_adamw_bf16state(const void* X, const void* dY, float* W,
+                                                   void* m_bf16, void* v_bf16, int64_t T,
+                                                   int64_t d_in, int64_t d_out,
+                                                   const forge_adamw_params* p, forge_tile tile,
+                                                   void* stream) {
+  if (forge_status s =
+          validate_wgrad_adamw_bf16state(X, dY, W, m_bf16, v_bf16, T, d_in, d_out, p, tile))
+    return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, W, static_cast<float*>(m_bf16), static_cast<float*>(v_bf16), T,
+                          d_in, d_out);
+  a.adam = make_adamw(*p);
+  return with_adamw_epi<DenseLaunch, EPI_ADAMW | EPI_BF16_STATE>(
+      *p, a, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_adamw_mixed(const void* grad, forge_dtype grad_dtype, float* W,
+                                         void* m, void* v, forge_dtype state_dtype, int64_t n,
+                                         const forge_adamw_params* p, void* stream) {
+  if (forge_status s = validate_adamw_mixed(grad, grad_dtype, W, m, v, state_dtype, n, p))
+    return s;
+  if (n == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  (void)hipGetLastError();
+  return with_adamw_epi<ElementwiseAdamW>(*p, grad, grad_dtype == FORGE_BF16, W, m, v,
+                                          state_dtype == FORGE_BF16, n, make_adamw(*p),
+                                          static_cast<hipStream_t>(stream));
+}
+
 FORGE_API const char* forge_status_string(forge_status s) {
   switch (s) {
     case FORGE_OK: return "ok";
@@ -371,6 +428,7 @@ FORGE_API const char* forge_status_string(forge_status s) {
     case FORGE_ERR_TILE: return "unknown tile id";
     case FORGE_ERR_DEVICE: return "no gfx950 device is current";
     case FORGE_ERR_LAUNCH: return "kernel launch failed";
+    case FORGE_ERR_DTYPE: return "unknown element type";
     default: return "unknown status";
   }
 }

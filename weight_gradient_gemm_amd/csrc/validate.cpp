@@ -39,8 +39,17 @@ forge_status check_tile(forge_tile tile) {
   return (tile >= 0 && tile < FORGE_TILE_COUNT) ? FORGE_OK : FORGE_ERR_TILE;
 }
 
+int dtype_bytes(forge_dtype t) { return t == FORGE_F32 ? 4 : (t == FORGE_BF16 ? 2 : 0); }
+
 forge_status check_dense(const void* X, const void* dY, const void* const* outs, int n_outs,
                          int64_t T, int64_t d_in, int64_t d_out) {
+  const int four[6] = {4, 4, 4, 4, 4, 4};
+  return check_dense_sized(X, dY, outs, four, n_outs, T, d_in, d_out);
+}
+
+forge_status check_dense_sized(const void* X, const void* dY, const void* const* outs,
+                               const int* elem_bytes, int n_outs, int64_t T, int64_t d_in,
+                               int64_t d_out) {
   if (T < 0 || d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
   const bool empty_out = d_in == 0 || d_out == 0;
   if (!empty_out) {
@@ -58,8 +67,8 @@ forge_status check_dense(const void* X, const void* dY, const void* const* outs,
 
   Span spans[6] = {};
   int n = 0;
-  const uint64_t state_bytes = uint64_t(d_in) * uint64_t(d_out) * 4u;
-  for (int k = 0; k < n_outs; ++k) spans[n++] = Span{outs[k], state_bytes};
+  const uint64_t elems = uint64_t(d_in) * uint64_t(d_out);
+  for (int k = 0; k < n_outs; ++k) spans[n++] = Span{outs[k], elems * uint64_t(elem_bytes[k])};
   if (forge_status s = check_outs_disjoint(spans, n)) return s;
   if (T > 0) {
     const Span sx{X, uint64_t(T) * uint64_t(d_in) * 2u}, sy{dY, uint64_t(T) * uint64_t(d_out) * 2u};
@@ -88,6 +97,14 @@ forge_status check_sgdm_params(const forge_sgdm_params* p) {
 
 forge_status check_elementwise(const float* grad, const float* const* outs, int n_outs,
                                int64_t n) {
+  const void* o[4] = {};
+  const int four[4] = {4, 4, 4, 4};
+  for (int k = 0; k < n_outs; ++k) o[k] = outs[k];
+  return check_elementwise_sized(grad, 4, o, four, n_outs, n);
+}
+
+forge_status check_elementwise_sized(const void* grad, int grad_bytes, const void* const* outs,
+                                     const int* elem_bytes, int n_outs, int64_t n) {
   if (n < 0) return FORGE_ERR_SHAPE;
   if (n == 0) return FORGE_OK;
   if (!grad) return FORGE_ERR_NULL;
@@ -99,9 +116,9 @@ forge_status check_elementwise(const float* grad, const float* const* outs, int 
     if (!aligned16(outs[k])) return FORGE_ERR_ALIGN;
   Span spans[4] = {};
   int m = 0;
-  for (int k = 0; k < n_outs; ++k) spans[m++] = Span{outs[k], uint64_t(n) * 4u};
+  for (int k = 0; k < n_outs; ++k) spans[m++] = Span{outs[k], uint64_t(n) * uint64_t(elem_bytes[k])};
   if (forge_status s = check_outs_disjoint(spans, m)) return s;
-  const Span sg{grad, uint64_t(n) * 4u};
+  const Span sg{grad, uint64_t(n) * uint64_t(grad_bytes)};
   for (int k = 0; k < m; ++k)
     if (spans_overlap(spans[k], sg)) return FORGE_ERR_ALIAS;
   return FORGE_OK;
@@ -185,6 +202,38 @@ forge_status validate_sgdm(const float* grad, const float* W, const float* mom, 
   if (!p) return FORGE_ERR_NULL;
   if (forge_status s = check_elementwise(grad, outs, 2, n)) return s;
   return check_sgdm_params(p);
+}
+
+forge_status validate_wgrad_bf16(const void* X, const void* dY, const void* grad, int64_t T,
+                                 int64_t d_in, int64_t d_out, forge_tile tile) {
+  const void* outs[1] = {grad};
+  const int bytes[1] = {2};
+  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 1, T, d_in, d_out)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_wgrad_adamw_bf16state(const void* X, const void* dY, const float* W,
+                                            const void* m, const void* v, int64_t T,
+                                            int64_t d_in, int64_t d_out,
+                                            const forge_adamw_params* p, forge_tile tile) {
+  const void* outs[3] = {W, m, v};
+  const int bytes[3] = {4, 2, 2};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 3, T, d_in, d_out)) return s;
+  if (forge_status s = check_adamw_params(p)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_adamw_mixed(const void* grad, forge_dtype grad_dtype, const float* W,
+                                  const void* m, const void* v, forge_dtype state_dtype,
+                                  int64_t n, const forge_adamw_params* p) {
+  const int gb = dtype_bytes(grad_dtype), sb = dtype_bytes(state_dtype);
+  const void* outs[3] = {W, m, v};
+  const int bytes[3] = {4, sb, sb};
+  if (!p) return FORGE_ERR_NULL;
+  if (gb == 0 || sb == 0) return FORGE_ERR_DTYPE;
+  if (forge_status s = check_elementwise_sized(grad, gb, outs, bytes, 3, n)) return s;
+  return check_adamw_params(p);
 }
 
 forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,

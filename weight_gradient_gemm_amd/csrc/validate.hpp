@@ -22,10 +22,18 @@ bool spans_overlap(const Span& a, const Span& b);
 
 forge_status check_dense(const void* X, const void* dY, const void* const* outs, int n_outs,
                          int64_t T, int64_t d_in, int64_t d_out);
+// As check_dense, with out k holding elem_bytes[k] bytes per element.
+forge_status check_dense_sized(const void* X, const void* dY, const void* const* outs,
+                               const int* elem_bytes, int n_outs, int64_t T, int64_t d_in,
+                               int64_t d_out);
+// Element size of a forge_dtype, or 0 if unknown.
+int dtype_bytes(forge_dtype t);
 forge_status check_adamw_params(const forge_adamw_params* p);
 forge_status check_sgdm_params(const forge_sgdm_params* p);
 forge_status check_tile(forge_tile tile);
 forge_status check_elementwise(const float* grad, const float* const* outs, int n_outs, int64_t n);
+forge_status check_elementwise_sized(const void* grad, int grad_bytes, const void* const* outs,
+                                     const int* elem_bytes, int n_outs, int64_t n);
 forge_status check_grouped(const void* X_perm, const void* dY_perm, const int64_t* offsets,
                            int32_t E, const void* const* outs, int n_outs, int64_t d_in,
                            int64_t d_out);
@@ -43,6 +51,15 @@ forge_status validate_adamw(const float* grad, const float* W, const float* m, c
                             int64_t n, const forge_adamw_params* p);
 forge_status validate_sgdm(const float* grad, const float* W, const float* mom, int64_t n,
                            const forge_sgdm_params* p);
+forge_status validate_wgrad_bf16(const void* X, const void* dY, const void* grad, int64_t T,
+                                 int64_t d_in, int64_t d_out, forge_tile tile);
+forge_status validate_wgrad_adamw_bf16state(const void* X, const void* dY, const float* W,
+                                            const void* m, const void* v, int64_t T,
+                                            int64_t d_in, int64_t d_out,
+                                            const forge_adamw_params* p, forge_tile tile);
+forge_status validate_adamw_mixed(const void* grad, forge_dtype grad_dtype, const float* W,
+                                  const void* m, const void* v, forge_dtype state_dtype,
+                                  int64_t n, const forge_adamw_params* p);
 forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
                                     const int64_t* offsets, int32_t E, const float* W,
                                     const float* m, const float* v, int64_t d_in, int64_t d_out,

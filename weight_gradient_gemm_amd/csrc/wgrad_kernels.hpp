@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "forge.h"
 #include "optim_math.hpp"
 
@@ -39,20 +41,34 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// EPI_ADAMW_EXACT is AdamW with eps = 0, where the square root must also be
-// exact on float32 denormals.
-enum Epi : int { EPI_ADAMW = 0, EPI_SGDM = 1, EPI_GRAD = 2, EPI_ADAMW_EXACT = 3 };
+// What the epilogue does with the accumulator: an optimizer or a gradient
+// store (low two bits), plus modifiers.
+enum Epi : int {
+  EPI_ADAMW = 0,
+  EPI_SGDM = 1,
+  EPI_GRAD = 2,
+  EPI_EXACT_SQRT = 4,   // AdamW with eps = 0: the square root must be exact on denormals
+  EPI_BF16_STATE = 8,   // AdamW m and v stored as bf16 (W stays float32)
+  EPI_BF16_OUT = 16,    // gradient store rounded to bf16
+};
 
-__host__ __device__ constexpr bool is_adamw(int epi) {
-  return epi == EPI_ADAMW || epi == EPI_ADAMW_EXACT;
+__host__ __device__ constexpr int epi_op(int epi) { return epi & 3; }
+__host__ __device__ constexpr bool is_adamw(int epi) { return epi_op(epi) == EPI_ADAMW; }
+// Bytes per element of the epilogue's arrays: W (or the stored gradient), then
+// the first and second optimizer state.
+__host__ __device__ constexpr int epi_w_bytes(int epi) {
+  return epi_op(epi) == EPI_GRAD && (epi & EPI_BF16_OUT) ? 2 : 4;
+}
+__host__ __device__ constexpr int epi_state_bytes(int epi) {
+  return is_adamw(epi) && (epi & EPI_BF16_STATE) ? 2 : 4;
 }
 
 struct WgradArgs {
   const uint16_t* X;   // [rows, d_in] bf16 bits
   const uint16_t* dY;  // [rows, d_out] bf16 bits
-  float* W;            // [(E,) d_out, d_in]; the gradient for EPI_GRAD
-  float* S1;           // m (AdamW) or momentum buffer (SGD)
-  float* S2;           // v (AdamW)
+  float* W;            // [(E,) d_out, d_in]; the gradient for EPI_GRAD (bf16 with EPI_BF16_OUT)
+  float* S1;           // m (AdamW) or momentum buffer (SGD); bf16 with EPI_BF16_STATE
+  float* S2;           // v (AdamW); bf16 with EPI_BF16_STATE
   int64_t T;           // tokens (dense calls)
   int32_t d_in;
   int32_t d_out;
@@ -156,6 +172,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window32(const void* base, uin
                                            0x00020000);
 }
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// float32 <-> bf16 for 4 elements (round to nearest even, as the hardware
+// conversion does).
+__device__ __forceinline__ u32x2_t pack_bf16x4(const f32x4_t& v) {
+  return __builtin_bit_cast(u32x2_t, __builtin_convertvector(v, bf16x4_t));
+}
+__device__ __forceinline__ f32x4_t unpack_bf16x4(const u32x2_t& u) {
+  return __builtin_convertvector(__builtin_bit_cast(bf16x4_t, u), f32x4_t);
+}
+
 // Optimizer state is streamed once per step: non-temporal cache policy.
 constexpr int kStatePolicy = 2;
 
@@ -168,6 +196,26 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 __device__ __forceinline__ f32x4_t load16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(
       f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kStatePolicy));
+}
+
+// Four consecutive elements of a float32 (ES = 4) or bf16 (ES = 2) array.
+template <int ES>
+__device__ __forceinline__ f32x4_t load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (ES == 4) {
+    return load16f(r, voff, soff);
+  } else {
+    return unpack_bf16x4(__builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kStatePolicy)));
+  }
+}
+template <int ES>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                       const f32x4_t& v) {
+  if constexpr (ES == 4) {
+    store16(r, voff, soff, v);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(v), r, (int)voff, (int)soff, kStatePolicy);
+  }
 }
 
 // s_waitcnt immediate (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt in
@@ -222,14 +270,18 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
                                          int lane, float* ep) {
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM;
   constexpr int LD = WM + 4;                 // floats per LDS row
-  constexpr int LPR = WM / 4;                // lanes per row (float4 each)
+  constexpr int LPR = WM / 4;                // lanes per row (4 elements each)
   constexpr int RPI = 64 / LPR;              // rows per instruction
   constexpr int NI = 32 / RPI;               // instructions per 32-column block
   constexpr int B = NI < 4 ? NI : 4;         // instructions per unit
   constexpr int UPB = NI / B;                // units per block
   constexpr int U = TN * UPB;
   constexpr int D = 2;                       // units in flight
-  constexpr int NS = is_adamw(EPI) ? 3 : (EPI == EPI_SGDM ? 2 : 0);   // state arrays read
+  constexpr int OP = epi_op(EPI);
+  constexpr int NS = OP == EPI_ADAMW ? 3 : (OP == EPI_SGDM ? 2 : 0);   // state arrays read
+  // Bytes per element of W (or the gradient), S1 and S2.
+  constexpr int ESW = epi_w_bytes(EPI), ESS = epi_state_bytes(EPI);
+  constexpr int ES[3] = {ESW, ESS, ESS};
   static_assert(NI % B == 0, "epilogue units must tile a block");
   static_assert(32 * LD * 4 <= C::STAGE * 2, "a wave's epilogue staging exceeds a slot");
 
@@ -237,13 +289,17 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   __syncthreads();                           // every wave is done with the operand ring
   const int r_lane = lane / LPR, c_lane = (lane % LPR) * 4;
   const int iw0 = i0 + wm * WM;
-  const uint32_t voff = iw0 + c_lane < d_in ? uint32_t(r_lane * d_in + c_lane) * 4u : kOOB;
-  const uint32_t inst_bytes = uint32_t(RPI) * uint32_t(d_in) * 4u;   // rows per instruction
-  float* const arr[3] = {W, S1, S2};
-  // Window over array k from the wave's first column of block n's first row.
+  const bool lane_ok = iw0 + c_lane < d_in;
+  const uint32_t elem = uint32_t(r_lane * d_in + c_lane);   // lane's first element in a block
+  char* const arr[3] = {reinterpret_cast<char*>(W), reinterpret_cast<char*>(S1),
+                        reinterpret_cast<char*>(S2)};
+  // Array k: the lane's byte offset, the bytes between row instructions, and
+  // the window from the wave's first column of block n's first row.
+  auto voff = [&](int k) { return lane_ok ? elem * uint32_t(ES[k]) : kOOB; };
+  auto inst_bytes = [&](int k) { return uint32_t(RPI) * uint32_t(d_in) * uint32_t(ES[k]); };
   auto block_window = [&](int k, int n) {
     const int64_t ob = int64_t(o0) + wn * C::WN + n * 32;
-    return window(arr[k] + ob * d_in + iw0, ((int64_t(d_out) - ob) * d_in - iw0) * 4);
+    return window(arr[k] + (ob * d_in + iw0) * ES[k], ((int64_t(d_out) - ob) * d_in - iw0) * ES[k]);
   };
   auto dump = [&](int n) {
     // Column-major: lane (o = lane % 32) writes rows 4 (lane / 32) + 8 q .. + 3.
@@ -263,7 +319,9 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
     for (int k = 0; k < NS; ++k) {
       const __amdgpu_buffer_rsrc_t r = block_window(k, n);
 #pragma unroll
-      for (int j = 0; j < B; ++j) st[u % D][j][k] = load16f(r, voff, (j0 + j) * inst_bytes);
+      for (int j = 0; j < B; ++j)
+        st[u % D][j][k] = k == 0 ? load4<ESW>(r, voff(k), (j0 + j) * inst_bytes(k))
+                                 : load4<ESS>(r, voff(k), (j0 + j) * inst_bytes(k));
     }
   };
 #pragma unroll
@@ -280,26 +338,27 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
     for (int j = 0; j < B; ++j)
       g[j] = *reinterpret_cast<const f32x4_t*>(ep + ((j0 + j) * RPI + r_lane) * LD + c_lane);
     const __amdgpu_buffer_rsrc_t rw = block_window(0, n);
-    if constexpr (EPI == EPI_GRAD) {
+    if constexpr (OP == EPI_GRAD) {
 #pragma unroll
-      for (int j = 0; j < B; ++j) store16(rw, voff, (j0 + j) * inst_bytes, g[j]);
-    } else if constexpr (is_adamw(EPI)) {
+      for (int j = 0; j < B; ++j) store4<ESW>(rw, voff(0), (j0 + j) * inst_bytes(0), g[j]);
+    } else if constexpr (OP == EPI_ADAMW) {
       const __amdgpu_buffer_rsrc_t r1 = block_window(1, n), r2 = block_window(2, n);
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         f32x4_t& s = st[u % D][j][0];
-        adamw_vec4<EPI == EPI_ADAMW_EXACT>(g[j], s, st[u % D][j][1], st[u % D][j][2], a.adam);
-        store16(rw, voff, (j0 + j) * inst_bytes, s);
-        store16(r1, voff, (j0 + j) * inst_bytes, st[u % D][j][1]);
-        store16(r2, voff, (j0 + j) * inst_bytes, st[u % D][j][2]);
+        adamw_vec4<(EPI & EPI_EXACT_SQRT) != 0>(g[j], s, st[u % D][j][1], st[u % D][j][2],
+                                                 a.adam);
+        store4<ESW>(rw, voff(0), (j0 + j) * inst_bytes(0), s);
+        store4<ESS>(r1, voff(1), (j0 + j) * inst_bytes(1), st[u % D][j][1]);
+        store4<ESS>(r2, voff(2), (j0 + j) * inst_bytes(2), st[u % D][j][2]);
       }
     } else {
       const __amdgpu_buffer_rsrc_t r1 = block_window(1, n);
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         sgdm_vec4(g[j], st[u % D][j][0], st[u % D][j][1], a.sgd);
-        store16(rw, voff, (j0 + j) * inst_bytes, st[u % D][j][0]);
-        store16(r1, voff, (j0 + j) * inst_bytes, st[u % D][j][1]);
+        store4<ESW>(rw, voff(0), (j0 + j) * inst_bytes(0), st[u % D][j][0]);
+        store4<ESS>(r1, voff(1), (j0 + j) * inst_bytes(1), st[u % D][j][1]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -624,31 +683,40 @@ void wgrad_persistent_kernel(WgradArgs a) {
 #undef FORGE_DECLARE_SLOTS
 
 // Unfused elementwise optimizers (the HBM-materialising comparison path).
-template <bool EXACT_SQRT>
-__global__ __launch_bounds__(256) void adamw_elementwise_kernel(const float* __restrict__ g,
+// AdamW reads a float32 or bf16 gradient and keeps m, v in float32 or bf16
+// (W is float32); the arithmetic is the fused epilogue's, in float32.
+template <bool EXACT_SQRT, bool GRAD_BF16, bool STATE_BF16>
+__global__ __launch_bounds__(256) void adamw_elementwise_kernel(const void* __restrict__ grad,
                                                                 float* __restrict__ W,
-                                                                float* __restrict__ m,
-                                                                float* __restrict__ v, int64_t n,
+                                                                void* __restrict__ m_,
+                                                                void* __restrict__ v_, int64_t n,
                                                                 AdamWConsts c) {
+  typedef typename std::conditional<GRAD_BF16, __bf16, float>::type GT;
+  typedef typename std::conditional<STATE_BF16, __bf16, float>::type ST;
+  typedef GT gt4 __attribute__((ext_vector_type(4)));
+  typedef ST st4 __attribute__((ext_vector_type(4)));
+  const GT* g = static_cast<const GT*>(grad);
+  ST* m = static_cast<ST*>(m_);
+  ST* v = static_cast<ST*>(v_);
   const int64_t n4 = n >> 2;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n4; k += stride) {
-    const f32x4_t gg = reinterpret_cast<const f32x4_t*>(g)[k];
+    const f32x4_t gg = __builtin_convertvector(reinterpret_cast<const gt4*>(g)[k], f32x4_t);
     f32x4_t w = reinterpret_cast<const f32x4_t*>(W)[k];
-    f32x4_t mm = reinterpret_cast<const f32x4_t*>(m)[k];
-    f32x4_t vv = reinterpret_cast<const f32x4_t*>(v)[k];
+    f32x4_t mm = __builtin_convertvector(reinterpret_cast<const st4*>(m)[k], f32x4_t);
+    f32x4_t vv = __builtin_convertvector(reinterpret_cast<const st4*>(v)[k], f32x4_t);
     adamw_vec4<EXACT_SQRT>(gg, w, mm, vv, c);
     reinterpret_cast<f32x4_t*>(W)[k] = w;
-    reinterpret_cast<f32x4_t*>(m)[k] = mm;
-    reinterpret_cast<f32x4_t*>(v)[k] = vv;
+    reinterpret_cast<st4*>(m)[k] = __builtin_convertvector(mm, st4);
+    reinterpret_cast<st4*>(v)[k] = __builtin_convertvector(vv, st4);
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
     const int64_t k = (n4 << 2) + threadIdx.x;
-    float w = W[k], mm = m[k], vv = v[k];
-    adamw_elem<EXACT_SQRT>(g[k], w, mm, vv, c);
+    float w = W[k], mm = float(m[k]), vv = float(v[k]);
+    adamw_elem<EXACT_SQRT>(float(g[k]), w, mm, vv, c);
     W[k] = w;
-    m[k] = mm;
-    v[k] = vv;
+    m[k] = ST(mm);
+    v[k] = ST(vv);
   }
 }
 
