@@ -35,6 +35,8 @@ from .ref import (  # noqa: F401
     adamw_step_mixed,
     bf16_bits_to_f64,
     bf16_round,
+    dgrad,
+    dgrad_f64,
     grouped_adamw_step,
     grouped_wgrad,
     sgdm_step,
@@ -42,4 +44,4 @@ from .ref import (  # noqa: F401
     wgrad_f64,
     wgrad_rows,
 )
-from .floor import StateFloor, acc_floor, acc_floor_rows  # noqa: F401
+from .floor import StateFloor, acc_floor, acc_floor_rows, dgrad_floor  # noqa: F401

@@ -32,6 +32,17 @@ def acc_floor(X_bits: np.ndarray, dY_bits: np.ndarray) -> np.ndarray:
     return 4.0 * U32 * np.sqrt(max(T, 1)) * np.sqrt(s2)
 
 
+def dgrad_floor(dY_bits: np.ndarray, W) -> np.ndarray:
+    """tau of the input gradient dX = dY W_b (a float32 sum over the d_out
+    outputs), in dX's [T, d_in] layout (float64)."""
+    from .ref import bf16_round
+    Wb = bf16_round(np.asarray(W, dtype=np.float32)).astype(np.float64)
+    dY = bf16_bits_to_f64(dY_bits)
+    K = Wb.shape[0]
+    s2 = (dY * dY) @ (Wb * Wb)
+    return 4.0 * U32 * np.sqrt(max(K, 1)) * np.sqrt(s2)
+
+
 def acc_floor_rows(X_bits: np.ndarray, dY_bits: np.ndarray, rows) -> np.ndarray:
     rows = np.asarray(rows, dtype=np.int64)
     return acc_floor(X_bits, np.ascontiguousarray(dY_bits[:, rows]))

@@ -46,6 +46,10 @@ W, m, v), so the only input difference is the float32 accumulation floor tau.
   * the weight delta is judged as above (W is computed from the unrounded
     new moments on both sides); the epilogue consistency check needs the
     GPU's unrounded moments and applies only with float32 state.
+
+Input gradient dX = dY W_b (judge_dgrad): float32 output within the
+accumulation floor of the exact sum; bf16 output between the bf16 roundings
+of the exact sum minus and plus that floor.
 """
 from __future__ import annotations
 
@@ -53,8 +57,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .floor import U32, StateFloor
-from .ref import adamw_param, adamw_step_mixed, bf16_round
+from .floor import U32, StateFloor, dgrad_floor
+from .ref import adamw_param, adamw_step_mixed, bf16_round, dgrad_f64
 
 REL_STATE = 1e-4
 ABS_DW = 1e-3
@@ -232,4 +236,27 @@ def judge_adamw_mixed(step, W_prev, m_prev, v_prev, W_gpu, m_gpu, v_gpu, g_ref, 
         ok &= _check("epilogue", np.abs(_f64(W_gpu) - _f64(W_cons)),
                      np.full(d_gpu.shape, ABS_DW * lr), checks)
     checks["normwise_dW"] = normwise(d_gpu, d_ref)
+    return Report(bool(ok), checks)
+
+
+def judge_dgrad(dX_gpu, dY_bits, W_before, bf16_out: bool, rows=None) -> Report:
+    """dX (float32, or bf16 widened to float32) against the exact dY W_b,
+    W_b the bf16 rounding of the weight before the step; `rows`: the token
+    rows dX_gpu holds (all if None)."""
+    dY_bits = np.asarray(dY_bits)
+    if rows is not None:
+        dY_bits = dY_bits[np.asarray(rows, dtype=np.int64)]
+    ref = dgrad_f64(dY_bits, W_before)
+    tau = dgrad_floor(dY_bits, W_before)
+    checks = {}
+    if bf16_out:
+        lo, hi = bf16_bracket(ref - tau, ref + tau)
+        ok = _check_bracket("dX", dX_gpu, lo, hi, checks)
+        checks["dX_rounded_equal"] = float(np.mean(
+            _f64(dX_gpu) == _f64(bf16_round(ref.astype(np.float32)))))
+    else:
+        # the float32 rounding of the exact sum is within half an ulp of it
+        ulp = np.abs(ref) * 2.0 ** -24
+        ok = _check("dX", np.abs(_f64(dX_gpu) - ref), tau + ulp, checks)
+    checks["normwise"] = normwise(dX_gpu, ref)
     return Report(bool(ok), checks)

@@ -69,6 +69,29 @@ def wgrad_rows(X_bits: np.ndarray, dY_bits: np.ndarray, rows) -> np.ndarray:
     return (dY.T @ X).astype(F32)
 
 
+def dgrad_f64(dY_bits: np.ndarray, W) -> np.ndarray:
+    """The input gradient dX = dY W of the same linear layer, in float64, not
+    rounded: dX[t, i] = sum_o dY[t, o] * W_b[o, i], with W_b the weight
+    rounded to bf16 (the operand precision of the layer's bf16 matmuls; W is
+    the float32 master weight).
+
+    FORGE assessment, "Math verified, not asserted", P1: the update happens in
+    place, so dX must be formed from the weight as it was before the step (the
+    in-place dX-before-update hazard). Each bf16 x bf16 product is exact in
+    float64.
+    """
+    Wb = bf16_round(np.asarray(W, dtype=F32)).astype(np.float64)
+    dY = bf16_bits_to_f64(dY_bits)
+    if dY.shape[1] != Wb.shape[0]:
+        raise ValueError("dY has d_out columns, W has d_out rows")
+    return dY @ Wb
+
+
+def dgrad(dY_bits: np.ndarray, W) -> np.ndarray:
+    """dgrad_f64 rounded once to float32 (round to nearest, ties to even)."""
+    return dgrad_f64(dY_bits, W).astype(F32)
+
+
 def grouped_wgrad(X_perm_bits: np.ndarray, dY_perm_bits: np.ndarray, offsets,
                   rows=None) -> list:
     """Per-expert gradients: expert e contracts routed rows offsets[e]..offsets[e+1).
