@@ -9,7 +9,9 @@ Llama-3-8B MLP down projection (X [8192, 14336], dY [8192, 4096], fp32 W/m/v
 [4096, 14336]). The unfused pair (fp32 gradient stored, then elementwise AdamW)
 is timed beside it, then (dense AdamW workloads) two precision variants: fused
 AdamW with bf16 moments, and the bf16-rounded gradient stored and followed by
-elementwise AdamW; and the CPU oracle on a bounded sample.
+elementwise AdamW; the layer's input gradient dX = dY W and the whole backward
+(dX from the weight before the step, then the fused step); and the CPU oracle
+on a bounded sample.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -87,6 +89,8 @@ def main():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the precision-variant legs (dense AdamW workloads)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the input-gradient and whole-backward legs (dense AdamW)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -238,6 +242,33 @@ def main():
             log(f"[bench] {name}: {v_step:.4f} ms/step")
         del mb, vb, gb
 
+    backward = None
+    if not args.no_backward and opt == "adamw" and not grouped:
+        # The layer's input gradient dX = dY W_b (bf16 out) on its own, then the
+        # whole backward: dX from the weight before the step, then the fused step.
+        dX = torch.empty((case.T, case.d_in), device=dev, dtype=torch.bfloat16)
+
+        def dgrad_only(step, batch):
+            wg.forge_dgrad(batch[1], W, dX, tile=0)
+
+        def linear_backward(step, batch):
+            X, dY, _, _ = batch
+            wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=step, tile=args.tile, **hp)
+
+        d_step, d_kernel, _ = timed(dgrad_only, args.steps, args.warmup)
+        b_step, _, _ = timed(linear_backward, args.steps, args.warmup)
+        backward = {
+            "dgrad": {"ms_per_step": round(d_step, 5), "kernel_ms": round(d_kernel, 5),
+                      "tflops": round(flops / d_kernel / 1e9, 2),
+                      "frac_bf16_peak": round(flops / d_kernel / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      "alg_hbm_bytes": 2 * case.T * case.d_out + 4 * n_param
+                      + 2 * case.T * case.d_in},
+            "linear_backward_adamw": {"ms_per_step": round(b_step, 5),
+                                      "tflops": round(2 * flops / b_step / 1e9, 2)},
+        }
+        log(f"[bench] dgrad: {d_step:.4f} ms/step; linear backward: {b_step:.4f} ms/step")
+        del dX
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         a = torch.ones(n, device=dev)
@@ -336,6 +367,7 @@ def main():
         "hbm_frac_alg": round(alg_bytes / ms_kernel / 1e6 / PEAK_HBM_GBS, 4),
         "unfused": unfused,
         "precision_variants": variants,
+        "backward": backward,
         "kernel_source_sha": sha,
         "cpu_baseline": cpu,
     }

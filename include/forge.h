@@ -255,6 +255,44 @@ FORGE_API forge_status forge_adamw_mixed(const void* grad, forge_dtype grad_dtyp
                                void* m, void* v, forge_dtype state_dtype, int64_t n,
                                const forge_adamw_params* p, void* stream);
 
+/*
+ * Input gradient of the same linear layer: dX = dY W_b, W_b the float32
+ * weight rounded to bf16 (nearest even) as the operand of a bf16 MFMA
+ * contraction over the d_out outputs, accumulated in float32 and stored as
+ * dX_dtype (FORGE_BF16: rounded to nearest even; FORGE_F32).
+ *   dY [T, d_out] bf16, W [d_out, d_in] float32 (read only), dX [T, d_in]
+ *   of dX_dtype, overwritten; all row-major, 16-byte aligned; d_in and d_out
+ *   multiples of 8. dX must not overlap dY or W. d_out == 0 writes zeros;
+ *   T == 0 or d_in == 0 writes nothing. tile: the tile ids above over
+ *   [d_in, T] (FORGE_TILE_PERSISTENT is treated as FORGE_TILE_256x256).
+ * Like the weight gradient, every tiling gives the same bits.
+ */
+FORGE_API forge_status forge_dgrad(const void* dY, const float* W, void* dX, forge_dtype dX_dtype,
+                         int64_t T, int64_t d_in, int64_t d_out, forge_tile tile,
+                         void* stream);
+
+/*
+ * Whole backward of a linear layer with the optimizer fused: forge_dgrad
+ * from the weight as it is on entry, then forge_wgrad_adamw (or _sgdm),
+ * stream-ordered on `stream`, so dX never sees the updated weight. FORGE
+ * assessment, "Math verified, not asserted", P1: the fused step updates W
+ * in place, so a dX formed after it would read the new weight (the in-place
+ * dX-before-update hazard); this call fixes the order. `tile` applies to the
+ * fused step; the dX contraction uses its default tile. Arguments as in the
+ * two calls; dX must also stay clear of X and the optimizer state. Every
+ * argument is validated before anything is launched; if the second launch
+ * fails, dX has been written and W and its state are unchanged.
+ */
+FORGE_API forge_status forge_linear_backward_adamw(const void* X, const void* dY, float* W,
+                                         float* m, float* v, void* dX, forge_dtype dX_dtype,
+                                         int64_t T, int64_t d_in, int64_t d_out,
+                                         const forge_adamw_params* p, forge_tile tile,
+                                         void* stream);
+FORGE_API forge_status forge_linear_backward_sgdm(const void* X, const void* dY, float* W,
+                                        float* mom, void* dX, forge_dtype dX_dtype, int64_t T,
+                                        int64_t d_in, int64_t d_out, const forge_sgdm_params* p,
+                                        forge_tile tile, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 FORGE_API const char* forge_status_string(forge_status s);
 

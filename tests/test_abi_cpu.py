@@ -34,9 +34,10 @@ def declared_symbols(root):
 
 def test_every_declared_symbol_is_exported(lib, root):
     names = declared_symbols(root)
-    assert names == sorted(["forge_adamw", "forge_adamw_mixed", "forge_grouped_wgrad_adamw",
-                            "forge_sgdm", "forge_status_string", "forge_wgrad",
-                            "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
+    assert names == sorted(["forge_adamw", "forge_adamw_mixed", "forge_dgrad",
+                            "forge_grouped_wgrad_adamw", "forge_linear_backward_adamw",
+                            "forge_linear_backward_sgdm", "forge_sgdm", "forge_status_string",
+                            "forge_wgrad", "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
                             "forge_wgrad_bf16", "forge_wgrad_sgdm"])
     for n in names:
         assert hasattr(lib, n), n
@@ -122,6 +123,11 @@ def test_no_gpu_means_device_error(lib):
     assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, C, 64, 64, 32,
                                            ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_adamw_mixed(A, 1, B, C, D, 1, 100, ctypes.byref(adam()), None) == 8
+    assert lib.forge_dgrad(Y_ADDR, A, B, 1, 64, 64, 32, 0, None) == 8
+    assert lib.forge_linear_backward_adamw(X_ADDR, Y_ADDR, A, B, C, D, 1, 64, 64, 32,
+                                           ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, 0, 64, 64, 32,
+                                          ctypes.byref(sgd()), 0, None) == 8
 
 
 def test_sgdm_and_unfused_reject(lib):
@@ -167,6 +173,44 @@ def test_precision_variants_reject(lib):
     p = adam(max_grad_norm=3.0)
     assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, C, 64, 64, 32, ctypes.byref(p),
                                            0, None) == 6
+
+
+def test_dgrad_and_linear_backward_reject(lib):
+    F32, BF16 = _lib.FORGE_F32, _lib.FORGE_BF16
+    T, d_in, d_out = 64, 64, 32
+    # dgrad: dY [T, d_out] bf16 at Y_ADDR, W [d_out, d_in] f32 at A, dX [T, d_in] at B
+    assert lib.forge_dgrad(Y_ADDR, A, B, 5, T, d_in, d_out, 0, None) == 10
+    assert lib.forge_dgrad(Y_ADDR, A, NULL, F32, T, d_in, d_out, 0, None) == 1
+    assert lib.forge_dgrad(NULL, A, B, F32, T, d_in, d_out, 0, None) == 1
+    assert lib.forge_dgrad(Y_ADDR, A, B, F32, -1, d_in, d_out, 0, None) == 2
+    assert lib.forge_dgrad(Y_ADDR, A, B, F32, T, 60, d_out, 0, None) == 3
+    assert lib.forge_dgrad(Y_ADDR, A, B + 4, F32, T, d_in, d_out, 0, None) == 3
+    # dX overlapping W (8 KiB of float32) or dY (4 KiB of bf16)
+    assert lib.forge_dgrad(Y_ADDR, A, A + 8192 - 16, BF16, T, d_in, d_out, 0, None) == 4
+    assert lib.forge_dgrad(Y_ADDR, A, A + 8192, BF16, T, d_in, d_out, 0, None) != 4
+    assert lib.forge_dgrad(Y_ADDR, A, Y_ADDR + 4096 - 16, F32, T, d_in, d_out, 0, None) == 4
+    assert lib.forge_dgrad(Y_ADDR, A, B, F32, T, d_in, d_out, 9, None) == 7
+    # nothing to write: no device needed
+    assert lib.forge_dgrad(Y_ADDR, A, NULL, F32, 0, d_in, d_out, 0, None) == 0
+    assert lib.forge_dgrad(Y_ADDR, A, NULL, F32, T, 0, d_out, 0, None) == 0
+
+    def lb(dX=D, dt=BF16, X=X_ADDR, p=None, tile=0, m=B, v=C):
+        p = adam() if p is None else p
+        return lib.forge_linear_backward_adamw(X, Y_ADDR, A, m, v, dX, dt, T, d_in, d_out,
+                                               ctypes.byref(p), tile, None)
+
+    assert lb(dt=3) == 10
+    assert lb(dX=NULL) == 1
+    assert lb(p=adam(max_grad_norm=1.0)) == 6
+    assert lb(tile=11) == 7
+    assert lb(m=A) == 4                       # state overlaps W (wgrad checks first)
+    assert lb(dX=B + 16) == 4                 # dX overlaps m
+    assert lb(dX=X_ADDR + 16) == 4            # dX overlaps X
+    assert lb(dX=A + 64) == 4                 # dX overlaps W
+    assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, B + 32, F32, T, d_in, d_out,
+                                          ctypes.byref(sgd()), 0, None) == 4
+    assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, F32, T, d_in, d_out,
+                                          ctypes.byref(sgd(momentum=2.0)), 0, None) == 5
 
 
 def test_grouped_rejects(lib):

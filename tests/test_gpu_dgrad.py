@@ -1,0 +1,164 @@
+"""GPU parity of the input gradient dX = dY W_b and of the linear-backward
+calls that order it before the fused optimizer step (page "docs(audit): FORGE
+assessment + residency-aware epilogue-fusion track", section "Math verified,
+not asserted", P1: the in-place dX-before-update hazard).
+
+Accuracy against the oracle's exact dY W_b (oracle.judge.judge_dgrad), every
+tiling bitwise equal, and the combined call bitwise equal to the two calls in
+the safe order.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import judge
+from synth import DenseCase
+from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
+                        host_f32, log, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wg():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_gradient_gemm_amd as wg
+    wg.library()
+    return wg
+
+
+def _sync():
+    torch_mod().cuda.synchronize()
+
+
+# K = d_out tails: 200 = 6 stages + 8, 392 = 12 stages + 8, 8 = one partial stage
+CASES = [DenseCase("ragged_77x264x200", T=77, d_in=264, d_out=200, seed_base=60000),
+         DenseCase("tiles_300x520x392", T=300, d_in=520, d_out=392, seed_base=61000),
+         DenseCase("k8_130x136x8", T=130, d_in=136, d_out=8, seed_base=62000)]
+
+
+def _dx(dtype, T, d_in):
+    torch = torch_mod()
+    return torch.full((T, d_in), float("nan"), device="cuda", dtype=dtype)
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+def test_dgrad_against_oracle(wg, case, tile, bf16_out):
+    torch = torch_mod()
+    _, dYb = synth.dense_inputs(case, 1)
+    W0, _, _ = synth.dense_state(case)
+    log(f"[{case.name}] dgrad tile {tile} bf16_out={bf16_out}")
+    dX = _dx(torch.bfloat16 if bf16_out else torch.float32, case.T, case.d_in)
+    wg.forge_dgrad(bf16_dev(dYb), f32_dev(W0), dX, tile=tile)
+    _sync()
+    rep = judge.judge_dgrad(host_f32(dX), dYb, W0, bf16_out)
+    log(f"  {rep}")
+    assert rep.passed, str(rep)
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_dgrad_bitwise_across_tilings(wg, bf16_out):
+    torch = torch_mod()
+    case = CASES[1]
+    _, dYb = synth.dense_inputs(case, 2)
+    W0, _, _ = synth.dense_state(case)
+    dY, W = bf16_dev(dYb), f32_dev(W0)
+    outs = []
+    for tile in (1, 2, 3, 0, 1):
+        dX = _dx(torch.bfloat16 if bf16_out else torch.float32, case.T, case.d_in)
+        wg.forge_dgrad(dY, W, dX, tile=tile)
+        _sync()
+        outs.append(host_f32(dX))
+    assert all(bits_equal(o, outs[0]) for o in outs[1:])
+
+
+def test_dgrad_zero_outputs_writes_zeros(wg):
+    torch = torch_mod()
+    dY = torch.empty((40, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    for dtype in (torch.float32, torch.bfloat16):
+        dX = _dx(dtype, 40, 64)
+        wg.forge_dgrad(dY, W, dX)
+        _sync()
+        got = host_f32(dX)
+        assert np.all(got == 0) and not np.any(np.signbit(got))
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_linear_backward_adamw(wg, bf16_out):
+    """Three steps: dX from the weight before each step, W/m/v as the fused
+    step, and the whole bitwise the two calls in the safe order."""
+    torch = torch_mod()
+    case = CASES[0]
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    W2, m2, v2 = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp)
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    for t in (1, 2, 3):
+        Xb, dYb = synth.dense_inputs(case, t)
+        X, dY = bf16_dev(Xb), bf16_dev(dYb)
+        log(f"[{case.name}] linear backward adamw step {t} bf16_out={bf16_out}")
+        W_prev = host(W)
+        dX = _dx(dt, case.T, case.d_in)
+        wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=t, **hp)
+        # the same two steps issued separately, in the safe order
+        dX2 = _dx(dt, case.T, case.d_in)
+        wg.forge_dgrad(dY, W2, dX2)
+        wg.forge_wgrad_adamw(X, dY, W2, m2, v2, step=t, **hp)
+        # and the hazard: dX formed after the update
+        dX_late = _dx(dt, case.T, case.d_in)
+        wg.forge_dgrad(dY, W2, dX_late)
+        _sync()
+        rep = judge.judge_dgrad(host_f32(dX), dYb, W_prev, bf16_out)
+        log(f"  dX {rep}")
+        assert rep.passed, str(rep)
+        rep = par.step(t, oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W_prev, host(W),
+                       host(m), host(v))
+        log(f"  W {rep}")
+        assert rep.passed, str(rep)
+        assert bits_equal(host_f32(dX), host_f32(dX2))
+        assert bits_equal(host(W), host(W2)) and bits_equal(host(m), host(m2))
+        assert not judge.judge_dgrad(host_f32(dX_late), dYb, W_prev, bf16_out).passed
+
+
+def test_linear_backward_sgdm(wg):
+    torch = torch_mod()
+    case = CASES[1]
+    hp = dict(lr=case.lr, momentum=case.momentum, weight_decay=0.01)
+    W0, _, _ = synth.dense_state(case)
+    W, b = f32_dev(W0), f32_dev(np.zeros_like(W0))
+    par = SgdmParity(W0, np.zeros_like(W0), hp)
+    for t in (1, 2):
+        Xb, dYb = synth.dense_inputs(case, t)
+        log(f"[{case.name}] linear backward sgdm step {t}")
+        W_prev = host(W)
+        dX = _dx(torch.float32, case.T, case.d_in)
+        wg.forge_linear_backward_sgdm(bf16_dev(Xb), bf16_dev(dYb), W, b, dX, **hp)
+        _sync()
+        rep = judge.judge_dgrad(host(dX), dYb, W_prev, False)
+        assert rep.passed, str(rep)
+        rep = par.step(oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W_prev, host(W), host(b))
+        assert rep.passed, str(rep)
+
+
+def test_linear_backward_zero_tokens(wg):
+    """No tokens: dX is empty and the fused step is a decay step."""
+    torch = torch_mod()
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(630, (32, 64), 0.02)
+    m0 = synth.normal_f32(631, W0.shape, 0.1)
+    v0 = np.abs(synth.normal_f32(632, W0.shape, 0.01))
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=2, **hp)
+    _sync()
+    assert bits_equal(host(m), np.float32(0.9) * m0)

@@ -65,6 +65,34 @@ def test_mlp_down_bf16_state_and_bf16_gradient(wg):
     assert np.all((got >= lo) & (got <= hi))
 
 
+def test_mlp_down_linear_backward(wg):
+    """The whole layer backward at the MLP-down size, two steps: dX (bf16) on
+    sampled token rows from the weight before each step, and the fused AdamW
+    step on sampled rows of W."""
+    torch = torch_mod()
+    case = synth.dense_case(1)
+    rows = sample_rows(case.d_out)
+    tokens = sample_rows(case.T, bn=256, per_tile=2, extra=16, seed=1)
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp, rows=rows)
+    dX = torch.empty((case.T, case.d_in), device="cuda", dtype=torch.bfloat16)
+    for t in (1, 2):
+        Xb, dYb = synth.dense_inputs(case, t)
+        log(f"[{case.name}] linear backward step {t}")
+        W_before = host(W)
+        wg.forge_linear_backward_adamw(bf16_dev(Xb), bf16_dev(dYb), W, m, v, dX, step=t, **hp)
+        torch.cuda.synchronize()
+        rep = judge.judge_dgrad(host_f32(dX, tokens), dYb, W_before, True, rows=tokens)
+        log(f"  dX {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+        rep = par.step(t, oracle.wgrad_rows(Xb, dYb, rows), oracle.acc_floor_rows(Xb, dYb, rows),
+                       W_before[rows], host(W, rows), host(m, rows), host(v, rows))
+        log(f"  W {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+
+
 def test_qkv_adamw_and_sgdm(wg):
     """GQA QKV projection: T=16384, d_in=4096, d_out=6144; AdamW and SGD-momentum."""
     case = synth.dense_case(2)

@@ -18,7 +18,10 @@ from ._lib import (  # noqa: F401
     STATUS,
     forge_adamw,
     forge_adamw_mixed,
+    forge_dgrad,
     forge_grouped_wgrad_adamw,
+    forge_linear_backward_adamw,
+    forge_linear_backward_sgdm,
     forge_sgdm,
     forge_status_string,
     forge_wgrad,

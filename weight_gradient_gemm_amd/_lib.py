@@ -77,11 +77,18 @@ def library() -> ctypes.CDLL:
                                                     ctypes.POINTER(AdamWParams), _i32, _vp]
         lib.forge_adamw_mixed.argtypes = [_vp, _i32, _vp, _vp, _vp, _i32, _i64,
                                           ctypes.POINTER(AdamWParams), _vp]
+        lib.forge_dgrad.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]
+        lib.forge_linear_backward_adamw.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64,
+                                                    _i64, _i64, ctypes.POINTER(AdamWParams),
+                                                    _i32, _vp]
+        lib.forge_linear_backward_sgdm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
+                                                   _i64, ctypes.POINTER(SgdmParams), _i32, _vp]
         lib.forge_status_string.argtypes = [_i32]
         lib.forge_status_string.restype = ctypes.c_char_p
         for name in ("forge_wgrad_adamw", "forge_wgrad_sgdm", "forge_wgrad", "forge_adamw",
                      "forge_sgdm", "forge_grouped_wgrad_adamw", "forge_wgrad_bf16",
-                     "forge_wgrad_adamw_bf16state", "forge_adamw_mixed"):
+                     "forge_wgrad_adamw_bf16state", "forge_adamw_mixed", "forge_dgrad",
+                     "forge_linear_backward_adamw", "forge_linear_backward_sgdm"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -323,3 +330,54 @@ def forge_adamw_mixed(grad, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999, e
     _check(library().forge_adamw_mixed(_ptr(grad), gd, _ptr(W), _ptr(m), _ptr(v), sd,
                                        grad.numel(), ctypes.byref(p), _stream(stream)),
            "forge_adamw_mixed")
+
+
+def _dx_args(dY, W, dX):
+    """Shapes of the input-gradient contraction: dY [T, d_out] bf16, W
+    [d_out, d_in] float32, dX [T, d_in] float32 or bf16."""
+    torch = _torch()
+    _want(dY, torch.bfloat16, "dY")
+    _want(W, torch.float32, "W")
+    T, d_out = _shape2(dY, "dY")
+    d_out2, d_in = _shape2(W, "W")
+    if d_out2 != d_out:
+        raise ValueError(f"W has {d_out2} rows, dY has {d_out} columns")
+    if tuple(dX.shape) != (T, d_in):
+        raise ValueError(f"dX must have shape {(T, d_in)}, got {tuple(dX.shape)}")
+    code = _dtype_code(dX, "dX")
+    _want(dX, dX.dtype, "dX")
+    return T, d_in, d_out, code
+
+
+def forge_dgrad(dY, W, dX, *, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """dX <- dY W_b (W_b: W rounded to bf16), float32 accumulation, stored in dX's dtype."""
+    T, d_in, d_out, code = _dx_args(dY, W, dX)
+    _check(library().forge_dgrad(_ptr(dY), _ptr(W), _ptr(dX), code, T, d_in, d_out, int(tile),
+                                 _stream(stream)), "forge_dgrad")
+
+
+def forge_linear_backward_adamw(X, dY, W, m, v, dX, *, step, lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                                tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """dX <- dY W_b from the weight on entry, then the fused AdamW step on W, m, v."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in)
+    _, _, _, code = _dx_args(dY, W, dX)
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_linear_backward_adamw(_ptr(X), _ptr(dY), _ptr(W), _ptr(m), _ptr(v),
+                                                 _ptr(dX), code, T, d_in, d_out, ctypes.byref(p),
+                                                 int(tile), _stream(stream)),
+           "forge_linear_backward_adamw")
+
+
+def forge_linear_backward_sgdm(X, dY, W, mom, dX, *, lr=1e-3, momentum=0.9, weight_decay=0.0,
+                               max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """dX <- dY W_b from the weight on entry, then the fused SGD-momentum step."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("mom", mom),), d_out, d_in)
+    _, _, _, code = _dx_args(dY, W, dX)
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_linear_backward_sgdm(_ptr(X), _ptr(dY), _ptr(W), _ptr(mom), _ptr(dX),
+                                                code, T, d_in, d_out, ctypes.byref(p), int(tile),
+                                                _stream(stream)),
+           "forge_linear_backward_sgdm")

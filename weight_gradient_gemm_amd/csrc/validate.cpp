@@ -247,4 +247,63 @@ forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
   return check_tile(tile);
 }
 
+forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forge_dtype dX_dtype,
+                            int64_t T, int64_t d_in, int64_t d_out, forge_tile tile) {
+  const int xb = dtype_bytes(dX_dtype);
+  if (xb == 0) return FORGE_ERR_DTYPE;
+  if (T < 0 || d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
+  if (T == 0 || d_in == 0) return check_tile(tile);      // dX is empty
+  if (!dX) return FORGE_ERR_NULL;
+  if (d_out > 0 && (!dY || !W)) return FORGE_ERR_NULL;
+  if (T > kMaxTokens || d_in > kMaxDim || d_out > kMaxDim) return FORGE_ERR_SHAPE;
+  if ((d_in % 8) != 0 || (d_out % 8) != 0) return FORGE_ERR_ALIGN;
+  if (!aligned16(dX)) return FORGE_ERR_ALIGN;
+  if (d_out > 0 && (!aligned16(dY) || !aligned16(W))) return FORGE_ERR_ALIGN;
+  const Span sx{dX, uint64_t(T) * uint64_t(d_in) * uint64_t(xb)};
+  const Span sy{dY, uint64_t(T) * uint64_t(d_out) * 2u};
+  const Span sw{W, uint64_t(d_out) * uint64_t(d_in) * 4u};
+  if (spans_overlap(sx, sy) || spans_overlap(sx, sw)) return FORGE_ERR_ALIAS;
+  return check_tile(tile);
+}
+
+namespace {
+
+// The linear-backward calls: dX must also stay clear of X and the state
+// the fused step writes.
+forge_status check_dx_clear(const void* dX, forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                            int64_t d_out, const void* X, const void* const* state, int n) {
+  if (T == 0 || d_in == 0) return FORGE_OK;
+  const Span sx{dX, uint64_t(T) * uint64_t(d_in) * uint64_t(dtype_bytes(dX_dtype))};
+  if (spans_overlap(sx, Span{X, uint64_t(T) * uint64_t(d_in) * 2u})) return FORGE_ERR_ALIAS;
+  for (int k = 0; k < n; ++k)
+    if (spans_overlap(sx, Span{state[k], uint64_t(d_in) * uint64_t(d_out) * 4u}))
+      return FORGE_ERR_ALIAS;
+  return FORGE_OK;
+}
+
+}  // namespace
+
+forge_status validate_linear_backward_adamw(const void* X, const void* dY, const float* W,
+                                            const float* m, const float* v, const void* dX,
+                                            forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                            int64_t d_out, const forge_adamw_params* p,
+                                            forge_tile tile) {
+  if (forge_status s = validate_wgrad_adamw(X, dY, W, m, v, T, d_in, d_out, p, tile)) return s;
+  if (forge_status s = validate_dgrad(dY, W, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
+    return s;
+  const void* state[2] = {m, v};
+  return check_dx_clear(dX, dX_dtype, T, d_in, d_out, X, state, 2);
+}
+
+forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const float* W,
+                                           const float* mom, const void* dX, forge_dtype dX_dtype,
+                                           int64_t T, int64_t d_in, int64_t d_out,
+                                           const forge_sgdm_params* p, forge_tile tile) {
+  if (forge_status s = validate_wgrad_sgdm(X, dY, W, mom, T, d_in, d_out, p, tile)) return s;
+  if (forge_status s = validate_dgrad(dY, W, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
+    return s;
+  const void* state[1] = {mom};
+  return check_dx_clear(dX, dX_dtype, T, d_in, d_out, X, state, 1);
+}
+
 }  // namespace forge

@@ -60,6 +60,17 @@ forge_status validate_wgrad_adamw_bf16state(const void* X, const void* dY, const
 forge_status validate_adamw_mixed(const void* grad, forge_dtype grad_dtype, const float* W,
                                   const void* m, const void* v, forge_dtype state_dtype,
                                   int64_t n, const forge_adamw_params* p);
+forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forge_dtype dX_dtype,
+                            int64_t T, int64_t d_in, int64_t d_out, forge_tile tile);
+forge_status validate_linear_backward_adamw(const void* X, const void* dY, const float* W,
+                                            const float* m, const float* v, const void* dX,
+                                            forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                            int64_t d_out, const forge_adamw_params* p,
+                                            forge_tile tile);
+forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const float* W,
+                                           const float* mom, const void* dX, forge_dtype dX_dtype,
+                                           int64_t T, int64_t d_in, int64_t d_out,
+                                           const forge_sgdm_params* p, forge_tile tile);
 forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
                                     const int64_t* offsets, int32_t E, const float* W,
                                     const float* m, const float* v, int64_t d_in, int64_t d_out,

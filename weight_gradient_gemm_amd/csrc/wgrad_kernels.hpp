@@ -680,8 +680,6 @@ void wgrad_persistent_kernel(WgradArgs a) {
   }
 }
 
-#undef FORGE_DECLARE_SLOTS
-
 // Unfused elementwise optimizers (the HBM-materialising comparison path).
 // AdamW reads a float32 or bf16 gradient and keeps m, v in float32 or bf16
 // (W is float32); the arithmetic is the fused epilogue's, in float32.
