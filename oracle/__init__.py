@@ -14,7 +14,7 @@ ships AdamW and SGD only). Fusion changes where the gradient lives, not its
 value (section "Math verified, not asserted", P1), so the unfused definition
 is the reference for the fused kernels.
 
-The precision variants of P6 (a bf16-rounded gradient, bf16 moments) and the
+fp8 inputs (the paper's fp8 row in P6) are in ``lowp.py``. The precision variants of P6 (a bf16-rounded gradient, bf16 moments) and the
 float64 reference they are measured against are in ``ref.py`` too; the P6
 study itself in ``precision_study.py``.
 
@@ -44,4 +44,5 @@ from .ref import (  # noqa: F401
     wgrad_f64,
     wgrad_rows,
 )
+from .lowp import E4M3, E5M2, acc_floor_fp8, fp8_to_f64, wgrad_fp8, wgrad_fp8_f64  # noqa: F401
 from .floor import StateFloor, acc_floor, acc_floor_rows, dgrad_floor  # noqa: F401

@@ -10,6 +10,11 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     dense_case,
     dense_inputs,
+    dense_inputs_f32,
+    dense_inputs_fp8,
+    fp8_bits_from_f32,
+    fp8_inputs,
+    fp8_scale,
     dense_state,
     grouped_case,
     grouped_inputs,

@@ -75,6 +75,49 @@ def normal_bf16(seed: int, shape, std: float = 1.0) -> np.ndarray:
     return bf16_bits_from_f32(normal_f32(seed, shape, std))
 
 
+# fp8 (OCP) encodings: exponent bits, fraction bits, bias, largest finite code
+FP8_FORMATS = {"e4m3": (4, 3, 7, 0x7E), "e5m2": (5, 2, 15, 0x7B)}
+
+
+def _fp8_positive_values(fmt: str) -> np.ndarray:
+    """Values of the non-negative finite codes 0 .. largest, in code order."""
+    eb, fb, bias, top = FP8_FORMATS[fmt]
+    c = np.arange(top + 1)
+    e, f = c >> fb, c & ((1 << fb) - 1)
+    return np.where(e == 0, f / (1 << fb) * 2.0 ** (1 - bias),
+                    (1 + f / (1 << fb)) * np.exp2(e - float(bias)))
+
+
+def fp8_bits_from_f32(a: np.ndarray, fmt: str) -> np.ndarray:
+    """Encode float32 values as fp8 codes (uint8): nearest value, ties to the
+    even code, magnitudes past the largest finite value saturate to it."""
+    vals = _fp8_positive_values(fmt)
+    x = np.asarray(a, dtype=np.float64)
+    mag = np.minimum(np.abs(x), vals[-1])
+    hi = np.clip(np.searchsorted(vals, mag), 1, len(vals) - 1)
+    lo = hi - 1
+    dlo, dhi = mag - vals[lo], vals[hi] - mag
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code[mag == 0] = 0
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def fp8_scale(a: np.ndarray, fmt: str) -> float:
+    """Power-of-two per-tensor scale s with max |a| / s within the format."""
+    amax = float(np.max(np.abs(a))) if np.size(a) else 0.0
+    if amax == 0.0:
+        return 1.0
+    return float(2.0 ** np.ceil(np.log2(amax / _fp8_positive_values(fmt)[-1])))
+
+
+def fp8_inputs(X: np.ndarray, dY: np.ndarray, x_fmt: str = "e4m3", dy_fmt: str = "e5m2"):
+    """(X8, s_x, dY8, s_dy): per-tensor power-of-two scaling, then fp8 codes."""
+    sx, sdy = fp8_scale(X, x_fmt), fp8_scale(dY, dy_fmt)
+    return (fp8_bits_from_f32(np.asarray(X, np.float32) / np.float32(sx), x_fmt), sx,
+            fp8_bits_from_f32(np.asarray(dY, np.float32) / np.float32(sdy), dy_fmt), sdy)
+
+
 # --------------------------------------------------------------------------
 # workload descriptions
 # --------------------------------------------------------------------------
@@ -218,6 +261,19 @@ def dense_inputs(case: DenseCase, step: int):
     else:
         dY = normal_bf16(seed * 2 + 1, (case.T, case.d_out), case.dy_std)
     return X, dY
+
+
+def dense_inputs_f32(case: DenseCase, step: int):
+    """The float32 draws behind dense_inputs (before the bf16 encoding)."""
+    seed = case.input_seed(step)
+    X = normal_f32(seed * 2, (case.T, case.d_in), case.x_std)
+    dY = normal_f32(seed * 2 + 1, (case.T, case.d_out), case.dy_std)
+    return X, dY
+
+
+def dense_inputs_fp8(case: DenseCase, step: int, x_fmt: str = "e4m3", dy_fmt: str = "e5m2"):
+    """(X8, s_x, dY8, s_dy) from the same float32 draws as dense_inputs."""
+    return fp8_inputs(*dense_inputs_f32(case, step), x_fmt, dy_fmt)
 
 
 def dense_state(case: DenseCase):

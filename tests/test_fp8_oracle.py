@@ -1,0 +1,134 @@
+"""Pins of the fp8-input oracle (page "docs(audit): FORGE assessment +
+residency-aware epilogue-fusion track", section "Math verified, not
+asserted", P6: the paper's fp8 row) and of the seeded fp8 input encoding.
+
+The decoder is checked against hand-decoded codes of both OCP formats and
+against torch's float8 types over all 256 codes; the contraction against
+exact rational arithmetic; the floor against real float32 accumulation.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import lowp
+
+F32 = np.float32
+
+
+@pytest.mark.parametrize("fmt,code,value", [
+    ("e4m3", 0x38, 1.0), ("e4m3", 0x7E, 448.0), ("e4m3", 0xFE, -448.0),
+    ("e4m3", 0x08, 2.0 ** -6), ("e4m3", 0x07, 7 * 2.0 ** -9), ("e4m3", 0x01, 2.0 ** -9),
+    ("e4m3", 0x39, 1.125), ("e4m3", 0x40, 2.0), ("e4m3", 0x00, 0.0),
+    ("e5m2", 0x3C, 1.0), ("e5m2", 0x7B, 57344.0), ("e5m2", 0x04, 2.0 ** -14),
+    ("e5m2", 0x01, 2.0 ** -16), ("e5m2", 0x3D, 1.25), ("e5m2", 0xC0, -2.0),
+    ("e5m2", 0x7C, np.inf), ("e5m2", 0xFC, -np.inf),
+])
+def test_fp8_decode_hand_values(fmt, code, value):
+    assert lowp.fp8_to_f64(np.array([code], np.uint8), fmt)[0] == value
+
+
+@pytest.mark.parametrize("fmt,nans", [("e4m3", [0x7F, 0xFF]),
+                                      ("e5m2", [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF])])
+def test_fp8_decode_nans(fmt, nans):
+    got = lowp.fp8_to_f64(np.arange(256, dtype=np.uint8), fmt)
+    assert sorted(np.nonzero(np.isnan(got))[0].tolist()) == nans
+    assert np.signbit(lowp.fp8_to_f64(np.array([0x80], np.uint8), fmt)[0])
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", "float8_e4m3fn"), ("e5m2", "float8_e5m2")])
+def test_fp8_decode_matches_torch(fmt, tdt):
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, tdt):
+        pytest.skip(f"torch has no {tdt}")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(getattr(torch, tdt)).to(torch.float64).numpy()
+    got = lowp.fp8_to_f64(codes, fmt)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), codes[~same]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encoder_round_trips_every_finite_code(fmt):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = lowp.fp8_to_f64(codes, fmt)
+    fin = np.isfinite(vals)
+    back = synth.fp8_bits_from_f32(vals[fin].astype(F32), fmt)
+    assert np.array_equal(lowp.fp8_to_f64(back, fmt), vals[fin])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encoder_rounds_to_nearest(fmt):
+    x = synth.normal_f32(500, (20000,), 30.0)
+    got = lowp.fp8_to_f64(synth.fp8_bits_from_f32(x, fmt), fmt)
+    vals = lowp.fp8_to_f64(np.arange(256, dtype=np.uint8), fmt)
+    vals = vals[np.isfinite(vals)]
+    best = np.min(np.abs(vals[None, :] - np.clip(x, vals.min(), vals.max())[:, None]
+                         .astype(np.float64)), axis=1)
+    err = np.abs(got - np.clip(x, vals.min(), vals.max()))
+    assert np.all(err == best)
+
+
+def test_fp8_scale_is_a_power_of_two_that_fits():
+    x = synth.normal_f32(501, (4096,), 3.0)
+    for fmt, top in (("e4m3", 448.0), ("e5m2", 57344.0)):
+        s = synth.fp8_scale(x, fmt)
+        assert np.log2(s) == np.round(np.log2(s))
+        assert np.max(np.abs(x)) / s <= top < 2 * np.max(np.abs(x)) / s
+
+
+@pytest.mark.parametrize("T,d_in,d_out,sx,sdy", [(1, 3, 2, 1.0, 1.0), (6, 4, 5, 0.25, 8.0),
+                                                 (9, 8, 3, 0.3, 1.7)])
+def test_wgrad_fp8_exact(T, d_in, d_out, sx, sdy):
+    rng = np.random.default_rng(T)
+    X8 = rng.integers(0, 256, (T, d_in), dtype=np.uint8)
+    dY8 = rng.integers(0, 256, (T, d_out), dtype=np.uint8)
+    X8[(X8 & 0x7F) == 0x7F] = 0x38                      # no NaN codes (e4m3)
+    dY8[(dY8 & 0x7C) == 0x7C] = 0x3C                    # no inf / NaN codes (e5m2)
+
+    def frac_e4m3(c):
+        s = -1 if c & 0x80 else 1
+        e, f = (c >> 3) & 15, c & 7
+        return s * (Fraction(f, 8) * Fraction(1, 64) if e == 0
+                    else (1 + Fraction(f, 8)) * Fraction(2) ** (e - 7))
+
+    def frac_e5m2(c):
+        s = -1 if c & 0x80 else 1
+        e, f = (c >> 2) & 31, c & 3
+        return s * (Fraction(f, 4) * Fraction(1, 2 ** 14) if e == 0
+                    else (1 + Fraction(f, 4)) * Fraction(2) ** (e - 15))
+
+    got = lowp.wgrad_fp8_f64(X8, "e4m3", sx, dY8, "e5m2", sdy)
+    for o in range(d_out):
+        for i in range(d_in):
+            q = sum((frac_e5m2(int(dY8[t, o])) * frac_e4m3(int(X8[t, i])) for t in range(T)),
+                    Fraction(0))
+            assert got[o, i] == pytest.approx(float(q) * sx * sdy, rel=1e-15, abs=1e-300)
+    assert got.shape == (d_out, d_in)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -7, 0.37])
+def test_fp8_floor_bounds_fp32_accumulation(scale):
+    X, dY = synth.normal_f32(510, (2048, 24)), synth.normal_f32(511, (2048, 16))
+    X8, sx, dY8, sdy = synth.fp8_inputs(X, dY)
+    sx = sx * scale
+    Xv = lowp.fp8_to_f64(X8, "e4m3").astype(F32)
+    Dv = lowp.fp8_to_f64(dY8, "e5m2").astype(F32)
+    acc = np.zeros((16, 24), F32)
+    for t0 in range(0, 2048, 16):                       # ascending chunks of 16, float32
+        acc = (acc + (Dv[t0:t0 + 16].T.astype(np.float64) @ Xv[t0:t0 + 16].astype(np.float64))
+               .astype(F32)).astype(F32)
+    g = acc * F32(sx * sdy)
+    err = np.abs(g.astype(np.float64) - lowp.wgrad_fp8_f64(X8, "e4m3", sx, dY8, "e5m2", sdy))
+    tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy)
+    assert np.all(err <= tau)
+
+
+def test_fp8_study_orders():
+    """fp8 inputs lose one to two orders of magnitude of gradient accuracy
+    against bf16 inputs (the paper's fp8 row is 44x worse than its baseline)."""
+    r = lowp.study()
+    assert 10 < r["ratio_grad"] < 100, r
+    assert r["ratio_update"] > 2, r
