@@ -7,9 +7,9 @@ resident in HBM: dW = X^T dY (bf16 in, fp32 accumulate, all tokens) consumed by
 AdamW in the epilogue, W/m/v updated in place. The default workload is a
 Llama-3-8B MLP down projection (X [8192, 14336], dY [8192, 4096], fp32 W/m/v
 [4096, 14336]). The unfused pair (fp32 gradient stored, then elementwise AdamW)
-is timed beside it, then (dense AdamW workloads) two precision variants: fused
+is timed beside it, then (dense AdamW workloads) three precision variants: fused
 AdamW with bf16 moments, and the bf16-rounded gradient stored and followed by
-elementwise AdamW; the layer's input gradient dX = dY W and the whole backward
+elementwise AdamW, and fused AdamW from fp8 inputs; the layer's input gradient dX = dY W and the whole backward
 (dX from the weight before the step, then the fused step); and the CPU oracle
 on a bounded sample.
 
@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused dW-GEMM+AdamW TFLOP/s & ms/step, MFMA util %, HBM bytes vs unfused"
 
@@ -229,18 +230,36 @@ def main():
             wg.forge_wgrad_bf16(X, dY, gb, tile=args.tile)
             wg.forge_adamw_mixed(gb, W, m, v, step=step, **hp)
 
+        # fp8 inputs (X E4M3, dY E5M2, power-of-two per-tensor scales) from the
+        # same float32 draws as the bf16 batches.
+        fp8_batches = []
+        for s_ in range(1, args.pool + 1):
+            X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, s_)
+            fp8_batches.append((torch.from_numpy(X8).to(dev), sx, torch.from_numpy(dY8).to(dev),
+                                sdy))
+
+        def fused_fp8(step, batch):
+            X8, sx, dY8, sdy = fp8_batches[(step - 1) % len(fp8_batches)]
+            wg.forge_wgrad_adamw_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, W, m, v, step=step,
+                                     tile=args.tile, **hp)
+
         variants = {}
         for name, fn, nbytes in (("fused_adamw_bf16_state", fused_bf16_state,
                                   x_bytes + 16 * n_param),
                                  ("bf16_gradient_then_adamw", bf16_grad_unfused,
-                                  x_bytes + 28 * n_param)):
+                                  x_bytes + 28 * n_param),
+                                 ("fused_adamw_fp8_inputs", fused_fp8,
+                                  x_bytes // 2 + 24 * n_param)):
             v_step, v_kernel, _ = timed(fn, args.steps, args.warmup)
             variants[name] = {"ms_per_step": round(v_step, 5),
                               "tflops": round(flops / v_step / 1e9, 2),
                               "alg_hbm_bytes": nbytes,
                               "frac_bf16_peak": round(flops / v_step / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            if "fp8" in name:
+                variants[name]["frac_fp8_peak"] = round(flops / v_step / 1e9 / PEAK_FP8_TFLOPS,
+                                                        4)
             log(f"[bench] {name}: {v_step:.4f} ms/step")
-        del mb, vb, gb
+        del mb, vb, gb, fp8_batches
 
     backward = None
     if not args.no_backward and opt == "adamw" and not grouped:

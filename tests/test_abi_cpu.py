@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(lib, root):
                             "forge_grouped_wgrad_adamw", "forge_linear_backward_adamw",
                             "forge_linear_backward_sgdm", "forge_sgdm", "forge_status_string",
                             "forge_wgrad", "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
-                            "forge_wgrad_bf16", "forge_wgrad_sgdm"])
+                            "forge_wgrad_adamw_fp8", "forge_wgrad_bf16", "forge_wgrad_fp8",
+                            "forge_wgrad_sgdm"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path], check=True,
@@ -124,6 +125,9 @@ def test_no_gpu_means_device_error(lib):
                                            ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_adamw_mixed(A, 1, B, C, D, 1, 100, ctypes.byref(adam()), None) == 8
     assert lib.forge_dgrad(Y_ADDR, A, B, 1, 64, 64, 32, 0, None) == 8
+    assert lib.forge_wgrad_fp8(X_ADDR, 2, 1.0, Y_ADDR, 3, 1.0, A, 64, 64, 32, 0, None) == 8
+    assert lib.forge_wgrad_adamw_fp8(X_ADDR, 2, 1.0, Y_ADDR, 3, 1.0, A, B, C, 64, 64, 32,
+                                     ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_linear_backward_adamw(X_ADDR, Y_ADDR, A, B, C, D, 1, 64, 64, 32,
                                            ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, 0, 64, 64, 32,
@@ -211,6 +215,34 @@ def test_dgrad_and_linear_backward_reject(lib):
                                           ctypes.byref(sgd()), 0, None) == 4
     assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, F32, T, d_in, d_out,
                                           ctypes.byref(sgd(momentum=2.0)), 0, None) == 5
+
+
+def test_fp8_rejects(lib):
+    E4, E5 = _lib.FORGE_FP8_E4M3, _lib.FORGE_FP8_E5M2
+
+    def g(xf=E4, sx=1.0, yf=E5, sy=1.0, grad=A, T=64, d_in=64, d_out=32, X=X_ADDR, tile=0):
+        return lib.forge_wgrad_fp8(X, xf, sx, Y_ADDR, yf, sy, grad, T, d_in, d_out, tile, None)
+
+    assert g(xf=_lib.FORGE_BF16) == 10
+    assert g(yf=7) == 10
+    assert g(sx=0.0) == 5
+    assert g(sy=-1.0) == 5
+    assert g(sx=float("nan")) == 5
+    assert g(sx=1e-30, sy=1e-30) == 5        # the product is not a normal float32
+    assert g(sx=1e30, sy=1e30) == 5          # the product overflows float32
+    assert g(d_in=72) == 3                   # fp8 rows need multiples of 16
+    assert g(d_out=40) == 3
+    assert g(grad=NULL) == 1
+    assert g(tile=9) == 7
+    # X8 is 1 byte per element: a gradient 64*64 bytes after X does not overlap it
+    assert g(grad=X_ADDR + 64 * 64) != 4
+    assert g(grad=X_ADDR + 64 * 64 - 16) == 4
+    assert lib.forge_wgrad_adamw_fp8(X_ADDR, E4, 1.0, Y_ADDR, E5, 1.0, A, B, C, 64, 64, 32,
+                                     ctypes.byref(adam(max_grad_norm=1.0)), 0, None) == 6
+    assert lib.forge_wgrad_adamw_fp8(X_ADDR, E4, 1.0, Y_ADDR, E5, 1.0, A, A, C, 64, 64, 32,
+                                     ctypes.byref(adam()), 0, None) == 4
+    assert lib.forge_wgrad_adamw_fp8(X_ADDR, E4, 1.0, Y_ADDR, E5, 1.0, A, B, C, 64, 64, 32,
+                                     None, 0, None) == 1
 
 
 def test_grouped_rejects(lib):

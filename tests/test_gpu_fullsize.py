@@ -93,6 +93,32 @@ def test_mlp_down_linear_backward(wg):
         assert rep.passed, f"step {t}: {rep}"
 
 
+def test_mlp_down_fp8_adamw(wg):
+    """fp8 inputs (X E4M3, dY E5M2, power-of-two per-tensor scales) at the
+    MLP-down size: the fused AdamW step for 3 steps on sampled rows of W."""
+    from oracle import lowp
+    torch = torch_mod()
+    case = synth.dense_case(1)
+    rows = sample_rows(case.d_out)
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp, rows=rows)
+    for t in range(1, 4):
+        X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, t)
+        log(f"[{case.name}] fp8 adamw step {t}")
+        W_prev = host(W, rows)
+        wg.forge_wgrad_adamw_fp8(torch.from_numpy(X8).to("cuda"), "e4m3", sx,
+                                 torch.from_numpy(dY8).to("cuda"), "e5m2", sdy, W, m, v, step=t,
+                                 **hp)
+        torch.cuda.synchronize()
+        g_ref = lowp.wgrad_fp8(X8, "e4m3", sx, np.ascontiguousarray(dY8[:, rows]), "e5m2", sdy)
+        tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows, exact_max=False)
+        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+
+
 def test_qkv_adamw_and_sgdm(wg):
     """GQA QKV projection: T=16384, d_in=4096, d_out=6144; AdamW and SGD-momentum."""
     case = synth.dense_case(2)

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     FORGE_TILE_DEFAULT,
     FORGE_BF16,
     FORGE_F32,
+    FORGE_FP8_E4M3,
+    FORGE_FP8_E5M2,
     ForgeError,
     STATUS,
     forge_adamw,
@@ -27,7 +29,9 @@ from ._lib import (  # noqa: F401
     forge_wgrad,
     forge_wgrad_adamw,
     forge_wgrad_adamw_bf16state,
+    forge_wgrad_adamw_fp8,
     forge_wgrad_bf16,
+    forge_wgrad_fp8,
     forge_wgrad_sgdm,
     library,
     library_path,

@@ -21,6 +21,8 @@ FORGE_TILE_PERSISTENT = 4
 
 FORGE_F32 = 0
 FORGE_BF16 = 1
+FORGE_FP8_E4M3 = 2
+FORGE_FP8_E5M2 = 3
 
 STATUS = {
     0: "FORGE_OK", 1: "FORGE_ERR_NULL", 2: "FORGE_ERR_SHAPE", 3: "FORGE_ERR_ALIGN",
@@ -83,12 +85,18 @@ def library() -> ctypes.CDLL:
                                                     _i32, _vp]
         lib.forge_linear_backward_sgdm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
                                                    _i64, ctypes.POINTER(SgdmParams), _i32, _vp]
+        _d = ctypes.c_double
+        lib.forge_wgrad_fp8.argtypes = [_vp, _i32, _d, _vp, _i32, _d, _vp, _i64, _i64, _i64,
+                                        _i32, _vp]
+        lib.forge_wgrad_adamw_fp8.argtypes = [_vp, _i32, _d, _vp, _i32, _d, _vp, _vp, _vp, _i64,
+                                              _i64, _i64, ctypes.POINTER(AdamWParams), _i32, _vp]
         lib.forge_status_string.argtypes = [_i32]
         lib.forge_status_string.restype = ctypes.c_char_p
         for name in ("forge_wgrad_adamw", "forge_wgrad_sgdm", "forge_wgrad", "forge_adamw",
                      "forge_sgdm", "forge_grouped_wgrad_adamw", "forge_wgrad_bf16",
                      "forge_wgrad_adamw_bf16state", "forge_adamw_mixed", "forge_dgrad",
-                     "forge_linear_backward_adamw", "forge_linear_backward_sgdm"):
+                     "forge_linear_backward_adamw", "forge_linear_backward_sgdm",
+                     "forge_wgrad_fp8", "forge_wgrad_adamw_fp8"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -381,3 +389,44 @@ def forge_linear_backward_sgdm(X, dY, W, mom, dX, *, lr=1e-3, momentum=0.9, weig
                                                 code, T, d_in, d_out, ctypes.byref(p), int(tile),
                                                 _stream(stream)),
            "forge_linear_backward_sgdm")
+
+
+_FP8 = {"e4m3": FORGE_FP8_E4M3, "e5m2": FORGE_FP8_E5M2}
+
+
+def _fp8_args(X8, x_fmt, dY8, dy_fmt):
+    """fp8 operands are uint8 tensors of codes; formats by name ("e4m3", "e5m2")."""
+    torch = _torch()
+    _want(X8, torch.uint8, "X8")
+    _want(dY8, torch.uint8, "dY8")
+    T, d_in = _shape2(X8, "X8")
+    T2, d_out = _shape2(dY8, "dY8")
+    if T2 != T:
+        raise ValueError(f"X8 has {T} token rows, dY8 has {T2}")
+    try:
+        return T, d_in, d_out, _FP8[x_fmt], _FP8[dy_fmt]
+    except KeyError as e:
+        raise ValueError(f"fp8 format must be one of {sorted(_FP8)}, got {e}") from None
+
+
+def forge_wgrad_fp8(X8, x_fmt, x_scale, dY8, dy_fmt, dy_scale, grad, *,
+                    tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """grad (float32) <- x_scale dy_scale dY8^T X8 from fp8 codes."""
+    T, d_in, d_out, xf, yf = _fp8_args(X8, x_fmt, dY8, dy_fmt)
+    _state_like(grad, (), d_out, d_in)
+    _check(library().forge_wgrad_fp8(_ptr(X8), xf, float(x_scale), _ptr(dY8), yf,
+                                     float(dy_scale), _ptr(grad), T, d_in, d_out, int(tile),
+                                     _stream(stream)), "forge_wgrad_fp8")
+
+
+def forge_wgrad_adamw_fp8(X8, x_fmt, x_scale, dY8, dy_fmt, dy_scale, W, m, v, *, step, lr=1e-3,
+                          beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
+                          max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """Fused weight gradient from fp8 inputs + AdamW on W, m, v in place."""
+    T, d_in, d_out, xf, yf = _fp8_args(X8, x_fmt, dY8, dy_fmt)
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in)
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_wgrad_adamw_fp8(_ptr(X8), xf, float(x_scale), _ptr(dY8), yf,
+                                           float(dy_scale), _ptr(W), _ptr(m), _ptr(v), T, d_in,
+                                           d_out, ctypes.byref(p), int(tile), _stream(stream)),
+           "forge_wgrad_adamw_fp8")

@@ -49,7 +49,7 @@ forge_status check_dense(const void* X, const void* dY, const void* const* outs,
 
 forge_status check_dense_sized(const void* X, const void* dY, const void* const* outs,
                                const int* elem_bytes, int n_outs, int64_t T, int64_t d_in,
-                               int64_t d_out) {
+                               int64_t d_out, int in_bytes) {
   if (T < 0 || d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
   const bool empty_out = d_in == 0 || d_out == 0;
   if (!empty_out) {
@@ -60,7 +60,9 @@ forge_status check_dense_sized(const void* X, const void* dY, const void* const*
   if (T > kMaxTokens || d_in > kMaxDim || d_out > kMaxDim) return FORGE_ERR_SHAPE;
   if (d_in * d_out > kMaxElems) return FORGE_ERR_SHAPE;
   if (empty_out) return FORGE_OK;
-  if ((d_in % 8) != 0 || (d_out % 8) != 0) return FORGE_ERR_ALIGN;
+  const int64_t mult = 16 / in_bytes;        // 16-byte chunks of a token row
+  if ((d_in % mult) != 0 || (d_out % mult) != 0 || (d_in % 8) != 0 || (d_out % 8) != 0)
+    return FORGE_ERR_ALIGN;
   for (int k = 0; k < n_outs; ++k)
     if (!aligned16(outs[k])) return FORGE_ERR_ALIGN;
   if (T > 0 && (!aligned16(X) || !aligned16(dY))) return FORGE_ERR_ALIGN;
@@ -71,7 +73,8 @@ forge_status check_dense_sized(const void* X, const void* dY, const void* const*
   for (int k = 0; k < n_outs; ++k) spans[n++] = Span{outs[k], elems * uint64_t(elem_bytes[k])};
   if (forge_status s = check_outs_disjoint(spans, n)) return s;
   if (T > 0) {
-    const Span sx{X, uint64_t(T) * uint64_t(d_in) * 2u}, sy{dY, uint64_t(T) * uint64_t(d_out) * 2u};
+    const Span sx{X, uint64_t(T) * uint64_t(d_in) * uint64_t(in_bytes)},
+        sy{dY, uint64_t(T) * uint64_t(d_out) * uint64_t(in_bytes)};
     for (int k = 0; k < n_outs; ++k)
       if (spans_overlap(spans[k], sx) || spans_overlap(spans[k], sy)) return FORGE_ERR_ALIAS;
   }
@@ -244,6 +247,47 @@ forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
   if (!p) return FORGE_ERR_NULL;
   if (forge_status s = check_grouped(X_perm, dY_perm, offsets, E, outs, 3, d_in, d_out)) return s;
   if (forge_status s = check_adamw_params(p)) return s;
+  return check_tile(tile);
+}
+
+namespace {
+
+bool is_fp8(forge_dtype t) { return t == FORGE_FP8_E4M3 || t == FORGE_FP8_E5M2; }
+
+// Per-tensor scales: finite and positive, with a float32 product that is too.
+forge_status check_fp8_scales(double x_scale, double dy_scale) {
+  if (!(std::isfinite(x_scale) && x_scale > 0.0 && std::isfinite(dy_scale) && dy_scale > 0.0))
+    return FORGE_ERR_HPARAM;
+  const float g = float(x_scale * dy_scale);
+  return std::isfinite(g) && g >= 1.17549435e-38f ? FORGE_OK : FORGE_ERR_HPARAM;
+}
+
+}  // namespace
+
+forge_status validate_wgrad_fp8(const void* X8, forge_dtype x_fmt, double x_scale,
+                                const void* dY8, forge_dtype dy_fmt, double dy_scale,
+                                const float* grad, int64_t T, int64_t d_in, int64_t d_out,
+                                forge_tile tile) {
+  if (!is_fp8(x_fmt) || !is_fp8(dy_fmt)) return FORGE_ERR_DTYPE;
+  const void* outs[1] = {grad};
+  const int bytes[1] = {4};
+  if (forge_status s = check_dense_sized(X8, dY8, outs, bytes, 1, T, d_in, d_out, 1)) return s;
+  if (forge_status s = check_fp8_scales(x_scale, dy_scale)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_wgrad_adamw_fp8(const void* X8, forge_dtype x_fmt, double x_scale,
+                                      const void* dY8, forge_dtype dy_fmt, double dy_scale,
+                                      const float* W, const float* m, const float* v, int64_t T,
+                                      int64_t d_in, int64_t d_out, const forge_adamw_params* p,
+                                      forge_tile tile) {
+  if (!is_fp8(x_fmt) || !is_fp8(dy_fmt)) return FORGE_ERR_DTYPE;
+  const void* outs[3] = {W, m, v};
+  const int bytes[3] = {4, 4, 4};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense_sized(X8, dY8, outs, bytes, 3, T, d_in, d_out, 1)) return s;
+  if (forge_status s = check_adamw_params(p)) return s;
+  if (forge_status s = check_fp8_scales(x_scale, dy_scale)) return s;
   return check_tile(tile);
 }
 

@@ -22,10 +22,11 @@ bool spans_overlap(const Span& a, const Span& b);
 
 forge_status check_dense(const void* X, const void* dY, const void* const* outs, int n_outs,
                          int64_t T, int64_t d_in, int64_t d_out);
-// As check_dense, with out k holding elem_bytes[k] bytes per element.
+// As check_dense, with out k holding elem_bytes[k] bytes per element and X,
+// dY in_bytes per element (fp8 inputs: 1, and d_in, d_out multiples of 16).
 forge_status check_dense_sized(const void* X, const void* dY, const void* const* outs,
                                const int* elem_bytes, int n_outs, int64_t T, int64_t d_in,
-                               int64_t d_out);
+                               int64_t d_out, int in_bytes = 2);
 // Element size of a forge_dtype, or 0 if unknown.
 int dtype_bytes(forge_dtype t);
 forge_status check_adamw_params(const forge_adamw_params* p);
@@ -60,6 +61,15 @@ forge_status validate_wgrad_adamw_bf16state(const void* X, const void* dY, const
 forge_status validate_adamw_mixed(const void* grad, forge_dtype grad_dtype, const float* W,
                                   const void* m, const void* v, forge_dtype state_dtype,
                                   int64_t n, const forge_adamw_params* p);
+forge_status validate_wgrad_fp8(const void* X8, forge_dtype x_fmt, double x_scale,
+                                const void* dY8, forge_dtype dy_fmt, double dy_scale,
+                                const float* grad, int64_t T, int64_t d_in, int64_t d_out,
+                                forge_tile tile);
+forge_status validate_wgrad_adamw_fp8(const void* X8, forge_dtype x_fmt, double x_scale,
+                                      const void* dY8, forge_dtype dy_fmt, double dy_scale,
+                                      const float* W, const float* m, const float* v, int64_t T,
+                                      int64_t d_in, int64_t d_out, const forge_adamw_params* p,
+                                      forge_tile tile);
 forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forge_dtype dX_dtype,
                             int64_t T, int64_t d_in, int64_t d_out, forge_tile tile);
 forge_status validate_linear_backward_adamw(const void* X, const void* dY, const float* W,

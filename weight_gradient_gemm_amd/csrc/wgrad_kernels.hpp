@@ -50,6 +50,7 @@ enum Epi : int {
   EPI_EXACT_SQRT = 4,   // AdamW with eps = 0: the square root must be exact on denormals
   EPI_BF16_STATE = 8,   // AdamW m and v stored as bf16 (W stays float32)
   EPI_BF16_OUT = 16,    // gradient store rounded to bf16
+  EPI_SCALE = 32,       // the accumulator times WgradArgs::gscale (scaled fp8 inputs)
 };
 
 __host__ __device__ constexpr int epi_op(int epi) { return epi & 3; }
@@ -78,6 +79,7 @@ struct WgradArgs {
   int32_t group_m;     // tile-order swizzle: tile rows per group
   AdamWConsts adam;
   SgdmConsts sgd;
+  float gscale;        // EPI_SCALE: factor applied to the accumulator once
 };
 
 struct GroupTable {
@@ -335,8 +337,10 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
     if (u % UPB == 0) dump(n);
     f32x4_t g[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j)
+    for (int j = 0; j < B; ++j) {
       g[j] = *reinterpret_cast<const f32x4_t*>(ep + ((j0 + j) * RPI + r_lane) * LD + c_lane);
+      if constexpr ((EPI & EPI_SCALE) != 0) g[j] = g[j] * a.gscale;
+    }
     const __amdgpu_buffer_rsrc_t rw = block_window(0, n);
     if constexpr (OP == EPI_GRAD) {
 #pragma unroll
