@@ -42,7 +42,8 @@ WORKLOADS = {
     "lm_head": (3, "adamw"),
     "moe": (4, "adamw"),
 }
-KERNEL_SOURCES = ("wgrad_kernels.hpp", "optim_math.hpp", "forge.hip")
+KERNEL_SOURCES = ("wgrad_kernels.hpp", "elementwise_kernels.hpp", "optim_math.hpp", "forge.hip",
+                  "host.hpp", "host.hip")
 
 
 def log(*a):

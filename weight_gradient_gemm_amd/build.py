@@ -44,16 +44,31 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
+# HIP translation units (compiled in parallel) and the host-only validation.
+HIP_UNITS = ("host.hip", "forge.hip", "forge_dgrad.hip", "forge_fp8.hip")
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link libforge.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
     v_obj = os.path.join(BUILD, "validate.o")
-    h_obj = os.path.join(BUILD, "forge.o")
-    _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "validate.cpp"), "-o", v_obj], verbose)
-    _run([_hipcc(), *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "forge.hip"), "-o", h_obj], verbose)
+    jobs = [["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "validate.cpp"), "-o", v_obj]]
+    objs = [v_obj]
+    for unit in HIP_UNITS:
+        obj = os.path.join(BUILD, unit.replace(".hip", ".o"))
+        jobs.append([_hipcc(), *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, unit), "-o", obj])
+        objs.append(obj)
+    procs = []
+    for cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+    failed = [cmd for cmd, pr in zip(jobs, procs) if pr.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp"
-    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", h_obj, v_obj, "-o", tmp], verbose)
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
