@@ -99,8 +99,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the fused kernel needs no collective, and "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the fused step needs no collective and no multi-GPU "
+              "path exists (run it with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
