@@ -368,6 +368,107 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   }
 }
 
+// AdamW epilogue for bf16 optimizer state. As epilogue(), but each lane owns
+// 8 consecutive columns of a row instead of 4, so m and v (8 bf16 = 16 bytes)
+// move in whole 16-byte accesses, like W (two per lane): 8 memory
+// instructions per 8 elements instead of 12, for a third fewer bytes.
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue_wide(const WgradArgs& a, f32x16_t (&acc)[C::TM][C::TN],
+                                              float* __restrict__ W, float* __restrict__ S1,
+                                              float* __restrict__ S2, int i0, int o0, int wm,
+                                              int wn, int lane, float* ep) {
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM;
+  constexpr int LD = WM + 4;                 // floats per LDS row
+  constexpr int LPR = WM / 8;                // lanes per row (8 elements each)
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+  constexpr int NI = 32 / RPI;               // instructions per 32-row block
+  constexpr int B = NI < 4 ? NI : 4;         // instructions per unit
+  constexpr int UPB = NI / B;
+  constexpr int U = TN * UPB;
+  constexpr int D = 2;                       // units in flight
+  static_assert(is_adamw(EPI) && (EPI & EPI_BF16_STATE), "bf16-state AdamW only");
+  static_assert(NI % B == 0, "epilogue units must tile a block");
+  static_assert(32 * LD * 4 <= C::STAGE * 2, "a wave's epilogue staging exceeds a slot");
+
+  const int d_in = a.d_in, d_out = a.d_out;
+  __syncthreads();                           // every wave is done with the operand ring
+  const int r_lane = lane / LPR, c_lane = (lane % LPR) * 8;
+  const int iw0 = i0 + wm * WM;
+  const bool lane_ok = iw0 + c_lane < d_in;  // d_in is a multiple of 8: all 8 or none
+  const uint32_t elem = uint32_t(r_lane * d_in + c_lane);
+  const uint32_t vw = lane_ok ? elem * 4u : kOOB, vs = lane_ok ? elem * 2u : kOOB;
+  const uint32_t iw = uint32_t(RPI) * uint32_t(d_in) * 4u, is = uint32_t(RPI) * uint32_t(d_in) * 2u;
+  auto block_window = [&](char* arr, int es, int n) {
+    const int64_t ob = int64_t(o0) + wn * C::WN + n * 32;
+    return window(arr + (ob * d_in + iw0) * es, ((int64_t(d_out) - ob) * d_in - iw0) * es);
+  };
+  char* const cw = reinterpret_cast<char*>(W);
+  char* const c1 = reinterpret_cast<char*>(S1);
+  char* const c2 = reinterpret_cast<char*>(S2);
+  auto dump = [&](int n) {
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t g = {acc[m][n][4 * q + 0], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2],
+                           acc[m][n][4 * q + 3]};
+        *reinterpret_cast<f32x4_t*>(ep + (lane & 31) * LD + m * 32 + 8 * q + 4 * (lane >> 5)) = g;
+      }
+  };
+  f32x4_t w[D][B][2];
+  u32x4_t mv[D][B][2];
+  auto issue = [&](int u) {
+    const int n = u / UPB, j0 = (u % UPB) * B;
+    const __amdgpu_buffer_rsrc_t rw = block_window(cw, 4, n), r1 = block_window(c1, 2, n),
+                                 r2 = block_window(c2, 2, n);
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      w[u % D][j][0] = load16f(rw, vw, (j0 + j) * iw);
+      w[u % D][j][1] = load16f(rw, vw + 16u, (j0 + j) * iw);
+      mv[u % D][j][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, (int)vs, (int)((j0 + j) * is),
+                                                              kStatePolicy);
+      mv[u % D][j][1] = __builtin_amdgcn_raw_buffer_load_b128(r2, (int)vs, (int)((j0 + j) * is),
+                                                              kStatePolicy);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D - 1 && u < U; ++u) issue(u);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u + D - 1 < U) issue(u + D - 1);
+    const int n = u / UPB, j0 = (u % UPB) * B;
+    if (u % UPB == 0) dump(n);
+    f32x4_t g[B][2];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        g[j][h] = *reinterpret_cast<const f32x4_t*>(ep + ((j0 + j) * RPI + r_lane) * LD + c_lane +
+                                                    4 * h);
+        if constexpr ((EPI & EPI_SCALE) != 0) g[j][h] = g[j][h] * a.gscale;
+      }
+    const __amdgpu_buffer_rsrc_t rw = block_window(cw, 4, n), r1 = block_window(c1, 2, n),
+                                 r2 = block_window(c2, 2, n);
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const u32x4_t mb = mv[u % D][j][0], vb = mv[u % D][j][1];
+      f32x4_t m0 = unpack_bf16x4(u32x2_t{mb[0], mb[1]}), m1 = unpack_bf16x4(u32x2_t{mb[2], mb[3]});
+      f32x4_t v0 = unpack_bf16x4(u32x2_t{vb[0], vb[1]}), v1 = unpack_bf16x4(u32x2_t{vb[2], vb[3]});
+      adamw_vec4<(EPI & EPI_EXACT_SQRT) != 0>(g[j][0], w[u % D][j][0], m0, v0, a.adam);
+      adamw_vec4<(EPI & EPI_EXACT_SQRT) != 0>(g[j][1], w[u % D][j][1], m1, v1, a.adam);
+      store16(rw, vw, (j0 + j) * iw, w[u % D][j][0]);
+      store16(rw, vw + 16u, (j0 + j) * iw, w[u % D][j][1]);
+      const u32x2_t pm0 = pack_bf16x4(m0), pm1 = pack_bf16x4(m1);
+      const u32x2_t pv0 = pack_bf16x4(v0), pv1 = pack_bf16x4(v1);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pm0[0], pm0[1], pm1[0], pm1[1]}, r1, (int)vs,
+                                             (int)((j0 + j) * is), kStatePolicy);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pv0[0], pv0[1], pv1[0], pv1[1]}, r2, (int)vs,
+                                             (int)((j0 + j) * is), kStatePolicy);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One output tile: mainloop over all tokens, then the epilogue.
 //
 // Staging: a buffer load with the LDS flag writes lane t's 16 bytes at
@@ -564,7 +665,10 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& a, const uint16_t* _
   // The epilogue starts with a full barrier, which also waits for the loads
   // of the zero stages still in flight.
   uint16_t* ep = wave == 0 ? sl.s0 : wave == 1 ? sl.s1 : wave == 2 ? sl.s2 : sl.s3;
-  epilogue<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, reinterpret_cast<float*>(ep));
+  if constexpr (is_adamw(EPI) && (EPI & EPI_BF16_STATE) != 0)
+    epilogue_wide<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, reinterpret_cast<float*>(ep));
+  else
+    epilogue<C, EPI>(a, acc, W, S1, S2, i0, o0, wm, wn, lane, reinterpret_cast<float*>(ep));
 }
 
 // The ring slots of a kernel, sized for its largest tile.
