@@ -9,9 +9,10 @@ Llama-3-8B MLP down projection (X [8192, 14336], dY [8192, 4096], fp32 W/m/v
 [4096, 14336]). The unfused pair (fp32 gradient stored, then elementwise AdamW)
 is timed beside it, then (dense AdamW workloads) three precision variants: fused
 AdamW with bf16 moments, and the bf16-rounded gradient stored and followed by
-elementwise AdamW, and fused AdamW from fp8 inputs; the layer's input gradient dX = dY W and the whole backward
-(dX from the weight before the step, then the fused step); and the CPU oracle
-on a bounded sample.
+elementwise AdamW, and fused AdamW from fp8 inputs; the layer's input gradient
+dX = dY W and the whole backward (dX from the weight before the step, then the
+fused step), each from the float32 weight and from the bf16 copy the fused step
+refreshes; and the CPU oracle on a bounded sample.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -266,28 +267,44 @@ def main():
     if not args.no_backward and opt == "adamw" and not grouped:
         # The layer's input gradient dX = dY W_b (bf16 out) on its own, then the
         # whole backward: dX from the weight before the step, then the fused step.
+        # Each from the float32 weight and from its bf16 copy (rounded once here;
+        # the fused step keeps it current).
         dX = torch.empty((case.T, case.d_in), device=dev, dtype=torch.bfloat16)
+        Wb = W.to(torch.bfloat16)
 
         def dgrad_only(step, batch):
             wg.forge_dgrad(batch[1], W, dX, tile=0)
+
+        def dgrad_copy(step, batch):
+            wg.forge_dgrad_bf16w(batch[1], Wb, dX, tile=0)
 
         def linear_backward(step, batch):
             X, dY, _, _ = batch
             wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=step, tile=args.tile, **hp)
 
-        d_step, d_kernel, _ = timed(dgrad_only, args.steps, args.warmup)
-        b_step, _, _ = timed(linear_backward, args.steps, args.warmup)
-        backward = {
-            "dgrad": {"ms_per_step": round(d_step, 5), "kernel_ms": round(d_kernel, 5),
-                      "tflops": round(flops / d_kernel / 1e9, 2),
-                      "frac_bf16_peak": round(flops / d_kernel / 1e9 / PEAK_BF16_TFLOPS, 4),
-                      "alg_hbm_bytes": 2 * case.T * case.d_out + 4 * n_param
-                      + 2 * case.T * case.d_in},
-            "linear_backward_adamw": {"ms_per_step": round(b_step, 5),
-                                      "tflops": round(2 * flops / b_step / 1e9, 2)},
-        }
-        log(f"[bench] dgrad: {d_step:.4f} ms/step; linear backward: {b_step:.4f} ms/step")
-        del dX
+        def linear_backward_copy(step, batch):
+            X, dY, _, _ = batch
+            wg.forge_linear_backward_adamw_bf16w(X, dY, W, m, v, Wb, dX, step=step,
+                                                 tile=args.tile, **hp)
+
+        dx_bytes = 2 * case.T * case.d_out + 2 * case.T * case.d_in
+        backward = {}
+        for name, fn, nbytes in (("dgrad", dgrad_only, dx_bytes + 4 * n_param),
+                                 ("dgrad_bf16_copy", dgrad_copy, dx_bytes + 2 * n_param)):
+            d_step, d_kernel, _ = timed(fn, args.steps, args.warmup)
+            backward[name] = {"ms_per_step": round(d_step, 5), "kernel_ms": round(d_kernel, 5),
+                              "tflops": round(flops / d_kernel / 1e9, 2),
+                              "frac_bf16_peak": round(flops / d_kernel / 1e9 / PEAK_BF16_TFLOPS,
+                                                      4),
+                              "alg_hbm_bytes": nbytes}
+            log(f"[bench] {name}: {d_step:.4f} ms/step")
+        for name, fn in (("linear_backward_adamw", linear_backward),
+                         ("linear_backward_adamw_bf16_copy", linear_backward_copy)):
+            b_step, _, _ = timed(fn, args.steps, args.warmup)
+            backward[name] = {"ms_per_step": round(b_step, 5),
+                              "tflops": round(2 * flops / b_step / 1e9, 2)}
+            log(f"[bench] {name}: {b_step:.4f} ms/step")
+        del dX, Wb
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4

@@ -296,6 +296,39 @@ FORGE_API forge_status forge_linear_backward_sgdm(const void* X, const void* dY,
                                         forge_tile tile, void* stream);
 
 /*
+ * The same with a bf16 working copy of the weight, the operand the layer's
+ * bf16 matmuls read (the dX order is P1's, as above). The copy is not from
+ * the pages, which keep W in float32 only: it is kept beside the float32
+ * master weight so that the dX contraction reads half the weight bytes and
+ * skips its float32-to-bf16 rounding pass; the fused step, which has the
+ * updated W in registers, refreshes it for 2 more bytes per element.
+ *   Wb [d_out, d_in]: bf16 (raw 16-bit storage), row-major, 16-byte aligned,
+ *   disjoint from every other argument.
+ * forge_dgrad_bf16w: dX = dY Wb; the bits of forge_dgrad when Wb holds W
+ * rounded to bf16 (nearest even). Contract otherwise as forge_dgrad.
+ * forge_linear_backward_adamw_bf16w / _sgdm_bf16w: dX from Wb as it is on
+ * entry, then the fused step on W and its state, which also stores the
+ * updated W rounded to bf16 (nearest even) into Wb, all stream-ordered on
+ * `stream`. If Wb holds bf16(W) on entry, dX, W and the state get the bits of
+ * forge_linear_backward_adamw (_sgdm), and Wb holds bf16(W) again on return:
+ * the caller rounds W once, before the first step. Contract otherwise as
+ * those calls.
+ */
+FORGE_API forge_status forge_dgrad_bf16w(const void* dY, const void* Wb, void* dX,
+                               forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
+                               forge_tile tile, void* stream);
+FORGE_API forge_status forge_linear_backward_adamw_bf16w(const void* X, const void* dY, float* W,
+                                               float* m, float* v, void* Wb, void* dX,
+                                               forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                               int64_t d_out, const forge_adamw_params* p,
+                                               forge_tile tile, void* stream);
+FORGE_API forge_status forge_linear_backward_sgdm_bf16w(const void* X, const void* dY, float* W,
+                                              float* mom, void* Wb, void* dX,
+                                              forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                              int64_t d_out, const forge_sgdm_params* p,
+                                              forge_tile tile, void* stream);
+
+/*
  * Weight gradient from fp8 inputs. FORGE assessment, "Math verified, not
  * asserted", P6: the paper's own fp8 row is 44x worse than its baseline;
  * these calls run that trade on the gfx950 fp8 matrix cores (twice the bf16

@@ -19,6 +19,7 @@ C = 0x400000000
 D = 0x600000000
 X_ADDR = 0x800000000
 Y_ADDR = 0xA00000000
+WB_ADDR = 0xC00000000
 
 
 @pytest.fixture(scope="module")
@@ -35,8 +36,10 @@ def declared_symbols(root):
 def test_every_declared_symbol_is_exported(lib, root):
     names = declared_symbols(root)
     assert names == sorted(["forge_adamw", "forge_adamw_mixed", "forge_dgrad",
-                            "forge_grouped_wgrad_adamw", "forge_linear_backward_adamw",
-                            "forge_linear_backward_sgdm", "forge_sgdm", "forge_status_string",
+                            "forge_dgrad_bf16w", "forge_grouped_wgrad_adamw",
+                            "forge_linear_backward_adamw", "forge_linear_backward_adamw_bf16w",
+                            "forge_linear_backward_sgdm", "forge_linear_backward_sgdm_bf16w",
+                            "forge_sgdm", "forge_status_string",
                             "forge_wgrad", "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
                             "forge_wgrad_adamw_fp8", "forge_wgrad_bf16", "forge_wgrad_fp8",
                             "forge_wgrad_sgdm"])
@@ -132,6 +135,11 @@ def test_no_gpu_means_device_error(lib):
                                            ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, 0, 64, 64, 32,
                                           ctypes.byref(sgd()), 0, None) == 8
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, B, 1, 64, 64, 32, 0, None) == 8
+    assert lib.forge_linear_backward_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, WB_ADDR, D, 1, 64, 64,
+                                                 32, ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, D, 0, 64, 64, 32,
+                                                ctypes.byref(sgd()), 0, None) == 8
 
 
 def test_sgdm_and_unfused_reject(lib):
@@ -215,6 +223,48 @@ def test_dgrad_and_linear_backward_reject(lib):
                                           ctypes.byref(sgd()), 0, None) == 4
     assert lib.forge_linear_backward_sgdm(X_ADDR, Y_ADDR, A, B, D, F32, T, d_in, d_out,
                                           ctypes.byref(sgd(momentum=2.0)), 0, None) == 5
+
+
+def test_bf16_weight_copy_calls_reject(lib):
+    F32, BF16 = _lib.FORGE_F32, _lib.FORGE_BF16
+    T, d_in, d_out = 64, 64, 32
+    # dgrad from Wb [d_out, d_in] bf16 (4 KiB) at WB_ADDR into dX at B
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, B, 5, T, d_in, d_out, 0, None) == 10
+    assert lib.forge_dgrad_bf16w(Y_ADDR, NULL, B, F32, T, d_in, d_out, 0, None) == 1
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR + 8, B, F32, T, d_in, d_out, 0, None) == 3
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, WB_ADDR + 4096 - 16, F32, T, d_in, d_out, 0,
+                                 None) == 4
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, WB_ADDR + 4096, BF16, T, d_in, d_out, 0,
+                                 None) != 4
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, B, F32, T, d_in, d_out, 9, None) == 7
+    assert lib.forge_dgrad_bf16w(Y_ADDR, WB_ADDR, NULL, F32, 0, d_in, d_out, 0, None) == 0
+
+    def lb(Wb=WB_ADDR, dX=D, dt=BF16, p=None, m=B, tile=0):
+        p = adam() if p is None else p
+        return lib.forge_linear_backward_adamw_bf16w(X_ADDR, Y_ADDR, A, m, C, Wb, dX, dt, T,
+                                                     d_in, d_out, ctypes.byref(p), tile, None)
+
+    assert lb(Wb=NULL) == 1
+    assert lb(dX=NULL) == 1
+    assert lb(dt=2) == 10
+    assert lb(Wb=WB_ADDR + 2) == 3
+    assert lb(Wb=A + 8192 - 16) == 4          # the copy overlaps W (8 KiB of float32)
+    assert lb(Wb=B + 16) == 4                 # the copy overlaps m
+    assert lb(Wb=X_ADDR + 16) == 4            # the copy overlaps X
+    assert lb(dX=WB_ADDR + 16) == 4           # dX overlaps the copy it reads
+    assert lb(dX=A + 64) == 4                 # dX overlaps W, which the step writes
+    assert lb(dX=C + 64) == 4                 # dX overlaps v
+    assert lb(p=adam(max_grad_norm=1.0)) == 6
+    assert lb(p=adam(beta2=1.5)) == 5
+    assert lb(tile=11) == 7
+    assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, A + 16, D, F32, T, d_in,
+                                                d_out, ctypes.byref(sgd()), 0, None) == 4
+    assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, D, F32, T, d_in,
+                                                d_out, ctypes.byref(sgd(momentum=2.0)), 0,
+                                                None) == 5
+    # nothing to write: no device needed
+    assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, D, F32, T, 0,
+                                                d_out, ctypes.byref(sgd()), 0, None) == 0
 
 
 def test_fp8_rejects(lib):

@@ -5,7 +5,9 @@ not asserted", P1: the in-place dX-before-update hazard).
 
 Accuracy against the oracle's exact dY W_b (oracle.judge.judge_dgrad), every
 tiling bitwise equal, and the combined call bitwise equal to the two calls in
-the safe order.
+the safe order. The bf16-copy calls (dX from a bf16 copy of W that the fused
+step refreshes) are held to the same bar, and the refreshed copy must be the
+oracle's nearest-even bf16 rounding of the updated W, bit for bit.
 """
 import numpy as np
 import pytest
@@ -162,3 +164,110 @@ def test_linear_backward_zero_tokens(wg):
     wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=2, **hp)
     _sync()
     assert bits_equal(host(m), np.float32(0.9) * m0)
+
+
+def _wb_dev(W):
+    """The caller's bf16 copy of a float32 weight, rounded once (the seeded
+    input encoder, nearest even)."""
+    return bf16_dev(synth.bf16_bits_from_f32(np.ascontiguousarray(W, dtype=np.float32)))
+
+
+def _copy_is_rounded(Wb, W) -> bool:
+    return bits_equal(host_f32(Wb), oracle.bf16_round(host(W)))
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+def test_dgrad_bf16w_against_oracle(wg, case, tile, bf16_out):
+    torch = torch_mod()
+    _, dYb = synth.dense_inputs(case, 3)
+    W0, _, _ = synth.dense_state(case)
+    log(f"[{case.name}] dgrad from the bf16 copy, tile {tile} bf16_out={bf16_out}")
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    dY = bf16_dev(dYb)
+    dX = _dx(dt, case.T, case.d_in)
+    wg.forge_dgrad_bf16w(dY, _wb_dev(W0), dX, tile=tile)
+    dX32 = _dx(dt, case.T, case.d_in)
+    wg.forge_dgrad(dY, f32_dev(W0), dX32, tile=tile)
+    _sync()
+    rep = judge.judge_dgrad(host_f32(dX), dYb, W0, bf16_out)
+    log(f"  {rep}")
+    assert rep.passed, str(rep)
+    assert bits_equal(host_f32(dX), host_f32(dX32))
+
+
+@pytest.mark.parametrize("tile", [0, 3, 4])
+@pytest.mark.parametrize("case", CASES[:2], ids=lambda c: c.name)
+def test_linear_backward_adamw_bf16w(wg, case, tile):
+    """Three steps from one initial rounding of W: dX from the copy, the fused
+    step judged against the oracle, the copy refreshed to bf16(W'), and all of
+    it bitwise the float32-weight call."""
+    torch = torch_mod()
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v, Wb = f32_dev(W0), f32_dev(m0), f32_dev(v0), _wb_dev(W0)
+    W2, m2, v2 = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp)
+    for t in (1, 2, 3):
+        Xb, dYb = synth.dense_inputs(case, 10 + t)
+        X, dY = bf16_dev(Xb), bf16_dev(dYb)
+        log(f"[{case.name}] linear backward adamw from the bf16 copy, tile {tile}, step {t}")
+        W_prev = host(W)
+        dX = _dx(torch.bfloat16, case.T, case.d_in)
+        wg.forge_linear_backward_adamw_bf16w(X, dY, W, m, v, Wb, dX, step=t, tile=tile, **hp)
+        dX2 = _dx(torch.bfloat16, case.T, case.d_in)
+        wg.forge_linear_backward_adamw(X, dY, W2, m2, v2, dX2, step=t, tile=tile, **hp)
+        _sync()
+        rep = judge.judge_dgrad(host_f32(dX), dYb, W_prev, True)
+        log(f"  dX {rep}")
+        assert rep.passed, str(rep)
+        rep = par.step(t, oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W_prev, host(W),
+                       host(m), host(v))
+        log(f"  W {rep}")
+        assert rep.passed, str(rep)
+        assert _copy_is_rounded(Wb, W)
+        assert bits_equal(host_f32(dX), host_f32(dX2))
+        assert bits_equal(host(W), host(W2)) and bits_equal(host(m), host(m2))
+        assert bits_equal(host(v), host(v2))
+
+
+def test_linear_backward_sgdm_bf16w(wg):
+    torch = torch_mod()
+    case = CASES[1]
+    hp = dict(lr=case.lr, momentum=case.momentum, weight_decay=0.01)
+    W0, _, _ = synth.dense_state(case)
+    W, b, Wb = f32_dev(W0), f32_dev(np.zeros_like(W0)), _wb_dev(W0)
+    par = SgdmParity(W0, np.zeros_like(W0), hp)
+    for t in (1, 2):
+        Xb, dYb = synth.dense_inputs(case, 20 + t)
+        log(f"[{case.name}] linear backward sgdm from the bf16 copy, step {t}")
+        W_prev = host(W)
+        dX = _dx(torch.float32, case.T, case.d_in)
+        wg.forge_linear_backward_sgdm_bf16w(bf16_dev(Xb), bf16_dev(dYb), W, b, Wb, dX, **hp)
+        _sync()
+        rep = judge.judge_dgrad(host(dX), dYb, W_prev, False)
+        assert rep.passed, str(rep)
+        rep = par.step(oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W_prev, host(W), host(b))
+        assert rep.passed, str(rep)
+        assert _copy_is_rounded(Wb, W)
+
+
+def test_linear_backward_bf16w_zero_tokens(wg):
+    """No tokens: dX is empty, the fused step decays W and still refreshes the
+    copy."""
+    torch = torch_mod()
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(640, (40, 64), 0.02)
+    m0 = synth.normal_f32(641, W0.shape, 0.1)
+    v0 = np.abs(synth.normal_f32(642, W0.shape, 0.01))
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    Wb = torch.zeros((40, 64), dtype=torch.bfloat16, device="cuda")
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty((0, 40), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    wg.forge_linear_backward_adamw_bf16w(X, dY, W, m, v, Wb, dX, step=2, **hp)
+    _sync()
+    assert bits_equal(host(m), np.float32(0.9) * m0)
+    assert _copy_is_rounded(Wb, W)
+    assert not bits_equal(host(W), W0)

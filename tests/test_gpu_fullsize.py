@@ -10,8 +10,8 @@ import pytest
 import oracle
 import synth
 from oracle import judge
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, f32_dev, host, host_f32, log,
-                        run_dense_adamw, run_dense_sgdm, sample_rows, torch_mod)
+from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, host_f32,
+                        log, run_dense_adamw, run_dense_sgdm, sample_rows, torch_mod)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -65,10 +65,12 @@ def test_mlp_down_bf16_state_and_bf16_gradient(wg):
     assert np.all((got >= lo) & (got <= hi))
 
 
-def test_mlp_down_linear_backward(wg):
+@pytest.mark.parametrize("copy", [False, True], ids=["f32_weight", "bf16_copy"])
+def test_mlp_down_linear_backward(wg, copy):
     """The whole layer backward at the MLP-down size, two steps: dX (bf16) on
     sampled token rows from the weight before each step, and the fused AdamW
-    step on sampled rows of W."""
+    step on sampled rows of W. With the bf16 copy, dX is read from it and the
+    refreshed copy is checked on the sampled rows."""
     torch = torch_mod()
     case = synth.dense_case(1)
     rows = sample_rows(case.d_out)
@@ -76,14 +78,21 @@ def test_mlp_down_linear_backward(wg):
     hp = adamw_hp(case)
     W0, m0, v0 = synth.dense_state(case)
     W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    Wb = bf16_dev(synth.bf16_bits_from_f32(W0)) if copy else None
     par = AdamWParity(W0, m0, v0, hp, rows=rows)
     dX = torch.empty((case.T, case.d_in), device="cuda", dtype=torch.bfloat16)
     for t in (1, 2):
         Xb, dYb = synth.dense_inputs(case, t)
-        log(f"[{case.name}] linear backward step {t}")
+        log(f"[{case.name}] linear backward step {t}, bf16 copy {copy}")
         W_before = host(W)
-        wg.forge_linear_backward_adamw(bf16_dev(Xb), bf16_dev(dYb), W, m, v, dX, step=t, **hp)
+        X, dY = bf16_dev(Xb), bf16_dev(dYb)
+        if copy:
+            wg.forge_linear_backward_adamw_bf16w(X, dY, W, m, v, Wb, dX, step=t, **hp)
+        else:
+            wg.forge_linear_backward_adamw(X, dY, W, m, v, dX, step=t, **hp)
         torch.cuda.synchronize()
+        if copy:
+            assert bits_equal(host_f32(Wb, rows), oracle.bf16_round(host(W, rows)))
         rep = judge.judge_dgrad(host_f32(dX, tokens), dYb, W_before, True, rows=tokens)
         log(f"  dX {rep}")
         assert rep.passed, f"step {t}: {rep}"

@@ -21,9 +21,12 @@ from ._lib import (  # noqa: F401
     forge_adamw,
     forge_adamw_mixed,
     forge_dgrad,
+    forge_dgrad_bf16w,
     forge_grouped_wgrad_adamw,
     forge_linear_backward_adamw,
+    forge_linear_backward_adamw_bf16w,
     forge_linear_backward_sgdm,
+    forge_linear_backward_sgdm_bf16w,
     forge_sgdm,
     forge_status_string,
     forge_wgrad,

@@ -85,6 +85,13 @@ def library() -> ctypes.CDLL:
                                                     _i32, _vp]
         lib.forge_linear_backward_sgdm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
                                                    _i64, ctypes.POINTER(SgdmParams), _i32, _vp]
+        lib.forge_dgrad_bf16w.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]
+        lib.forge_linear_backward_adamw_bf16w.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
+            ctypes.POINTER(AdamWParams), _i32, _vp]
+        lib.forge_linear_backward_sgdm_bf16w.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, ctypes.POINTER(SgdmParams),
+            _i32, _vp]
         _d = ctypes.c_double
         lib.forge_wgrad_fp8.argtypes = [_vp, _i32, _d, _vp, _i32, _d, _vp, _i64, _i64, _i64,
                                         _i32, _vp]
@@ -96,7 +103,8 @@ def library() -> ctypes.CDLL:
                      "forge_sgdm", "forge_grouped_wgrad_adamw", "forge_wgrad_bf16",
                      "forge_wgrad_adamw_bf16state", "forge_adamw_mixed", "forge_dgrad",
                      "forge_linear_backward_adamw", "forge_linear_backward_sgdm",
-                     "forge_wgrad_fp8", "forge_wgrad_adamw_fp8"):
+                     "forge_wgrad_fp8", "forge_wgrad_adamw_fp8", "forge_dgrad_bf16w",
+                     "forge_linear_backward_adamw_bf16w", "forge_linear_backward_sgdm_bf16w"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -340,16 +348,16 @@ def forge_adamw_mixed(grad, W, m, v, *, step, lr=1e-3, beta1=0.9, beta2=0.999, e
            "forge_adamw_mixed")
 
 
-def _dx_args(dY, W, dX):
+def _dx_args(dY, W, dX, w_name="W"):
     """Shapes of the input-gradient contraction: dY [T, d_out] bf16, W
-    [d_out, d_in] float32, dX [T, d_in] float32 or bf16."""
+    [d_out, d_in] float32 (Wb: bf16), dX [T, d_in] float32 or bf16."""
     torch = _torch()
     _want(dY, torch.bfloat16, "dY")
-    _want(W, torch.float32, "W")
+    _want(W, torch.bfloat16 if w_name == "Wb" else torch.float32, w_name)
     T, d_out = _shape2(dY, "dY")
-    d_out2, d_in = _shape2(W, "W")
+    d_out2, d_in = _shape2(W, w_name)
     if d_out2 != d_out:
-        raise ValueError(f"W has {d_out2} rows, dY has {d_out} columns")
+        raise ValueError(f"{w_name} has {d_out2} rows, dY has {d_out} columns")
     if tuple(dX.shape) != (T, d_in):
         raise ValueError(f"dX must have shape {(T, d_in)}, got {tuple(dX.shape)}")
     code = _dtype_code(dX, "dX")
@@ -389,6 +397,42 @@ def forge_linear_backward_sgdm(X, dY, W, mom, dX, *, lr=1e-3, momentum=0.9, weig
                                                 code, T, d_in, d_out, ctypes.byref(p), int(tile),
                                                 _stream(stream)),
            "forge_linear_backward_sgdm")
+
+
+def forge_dgrad_bf16w(dY, Wb, dX, *, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """dX <- dY Wb from a bf16 copy Wb of the weight, float32 accumulation."""
+    T, d_in, d_out, code = _dx_args(dY, Wb, dX, "Wb")
+    _check(library().forge_dgrad_bf16w(_ptr(dY), _ptr(Wb), _ptr(dX), code, T, d_in, d_out,
+                                       int(tile), _stream(stream)), "forge_dgrad_bf16w")
+
+
+def forge_linear_backward_adamw_bf16w(X, dY, W, m, v, Wb, dX, *, step, lr=1e-3, beta1=0.9,
+                                      beta2=0.999, eps=1e-8, weight_decay=0.01,
+                                      max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT,
+                                      stream=None) -> None:
+    """dX <- dY Wb from the bf16 copy on entry, then the fused AdamW step on W,
+    m, v, which also stores bf16(W) into Wb."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in)
+    _, _, _, code = _dx_args(dY, Wb, dX, "Wb")
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_linear_backward_adamw_bf16w(
+        _ptr(X), _ptr(dY), _ptr(W), _ptr(m), _ptr(v), _ptr(Wb), _ptr(dX), code, T, d_in, d_out,
+        ctypes.byref(p), int(tile), _stream(stream)), "forge_linear_backward_adamw_bf16w")
+
+
+def forge_linear_backward_sgdm_bf16w(X, dY, W, mom, Wb, dX, *, lr=1e-3, momentum=0.9,
+                                     weight_decay=0.0, max_grad_norm=0.0,
+                                     tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """dX <- dY Wb from the bf16 copy on entry, then the fused SGD-momentum
+    step, which also stores bf16(W) into Wb."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("mom", mom),), d_out, d_in)
+    _, _, _, code = _dx_args(dY, Wb, dX, "Wb")
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_linear_backward_sgdm_bf16w(
+        _ptr(X), _ptr(dY), _ptr(W), _ptr(mom), _ptr(Wb), _ptr(dX), code, T, d_in, d_out,
+        ctypes.byref(p), int(tile), _stream(stream)), "forge_linear_backward_sgdm_bf16w")
 
 
 _FP8 = {"e4m3": FORGE_FP8_E4M3, "e5m2": FORGE_FP8_E5M2}

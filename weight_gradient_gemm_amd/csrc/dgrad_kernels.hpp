@@ -17,6 +17,9 @@
 //   as float32 into registers, rounded to bf16 and written to LDS in the
 //   weight-gradient kernel's operand layout ([k][feature] rows, 16-byte chunk
 //   c of row r at c ^ 4 (r mod 4)), then gathered with LDS transpose reads.
+//   Given a bf16 copy of W instead (WB), the stage's rows go straight into
+//   that layout with direct-to-LDS loads, like the weight gradient's
+//   operands: half the bytes, and no register pass or LDS store instructions.
 //   B operand, dY [t][o] (o contiguous): 8 consecutive o of one token are
 //   already contiguous, so each stage goes straight into LDS as [token][o]
 //   rows of 64 bytes, chunk c of row r at c ^ ((r / 4) mod 4) so that the
@@ -32,12 +35,13 @@ namespace forge {
 // One dX^T tile. `a` is set up for the epilogue: a.W = dX, a.d_in = d_in (dX
 // row length), a.d_out = T (dX rows). K = the layer's d_out.
 //
-// Per stage s (32 outputs o): loads for stage s + 2 are issued (W into the
-// register set stage s used, dY straight into LDS slot (s + 2) % 4), so each
-// load has about a stage and a half of MFMA work to land.
-template <class C, int EPI>
+// Per stage s (32 outputs o): loads for stage s + 2 are issued (float32 W
+// into the register set stage s used, bf16 W and dY straight into LDS slot
+// (s + 2) % 4), so each load has about a stage and a half of MFMA work to land.
+// Wsrc: float32 W, or with WB its bf16 copy.
+template <class C, int EPI, bool WB>
 __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* __restrict__ dY,
-                                           const float* __restrict__ W, int K, int tile_m,
+                                           const void* __restrict__ Wsrc, int K, int tile_m,
                                            int tile_n, const Slots& sl) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
   constexpr int RBA = BM * 2;                       // bytes per LDS row of the A region
@@ -49,6 +53,14 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
   static_assert(NA >= 1 && NB >= 1 && (BK / RPI_A) % C::WAVES == 0 && (BN / 16) % C::WAVES == 0,
                 "stage loads split evenly over the waves");
   static_assert(BOFF + BN * 64 <= C::STAGE * 2, "stage exceeds a slot");
+  // bf16 W: 1 KB direct-to-LDS loads of RPQ rows (CPA 16-byte chunks each).
+  constexpr int CPA = BM / 8;
+  constexpr int RPQ = 64 / CPA;
+  constexpr int NQA = BK / RPQ / C::WAVES;          // bf16 W loads per wave per stage
+  static_assert(!WB || (NQA >= 1 && (BK / RPQ) % C::WAVES == 0), "bf16 W loads split evenly");
+  constexpr int NAL = WB ? NQA : NA;                // W load instructions per wave per stage
+  const float* __restrict__ W = static_cast<const float*>(Wsrc);
+  const uint16_t* __restrict__ Wh = static_cast<const uint16_t*>(Wsrc);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,6 +82,16 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
     const int r = RPI_A * (NA * wave + j) + a_row;
     a_lds[j] = uint32_t(r * RBA + (((a_col >> 3) ^ (4 * (r & 3))) << 4) + (a_col & 4) * 2);
   }
+  // bf16 W loads: instruction q = NQA wave + j writes LDS rows RPQ q ..
+  // RPQ q + RPQ - 1; lane l fills physical chunk l % CPA of row RPQ q + l / CPA,
+  // which holds logical chunk (l % CPA) ^ 4 (row mod 4). Columns past d_in read 0.
+  uint32_t h_voff[WB ? NQA : 1];
+#pragma unroll
+  for (int j = 0; j < (WB ? NQA : 1); ++j) {
+    const int lrow = lane / CPA, r = RPQ * (NQA * wave + j) + lrow;
+    const int ch = (lane % CPA) ^ (4 * (r & 3));
+    h_voff[j] = i0 + 8 * ch < d_in ? uint32_t(lrow * d_in + 8 * ch) * 2u : kOOB;
+  }
   // dY loads: instruction q = NB wave + j writes LDS rows 16 q .. 16 q + 15;
   // lane l fills row 16 q + l / 4, physical chunk l % 4, which holds logical
   // chunk c = (l % 4) ^ ((l / 16) % 4), i.e. outputs k0 + 8 c .. + 7.
@@ -83,17 +105,28 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
   auto issue = [&](uint16_t* slot, f32x4_t (&wr)[NA]) {
     const int k0 = g_stage * BK;
     const int rows_k = K - k0 < BK ? (K - k0 > 0 ? K - k0 : 0) : BK;
-    const __amdgpu_buffer_rsrc_t rw =
-        window32(W + int64_t(k0) * d_in + i0,
-                 rows_k > 0 ? uint32_t(rows_k * d_in - i0) * 4u : 0u);
     const __amdgpu_buffer_rsrc_t ry =
         window32(dY + t0 * K + k0, k0 < K ? uint32_t(rows_t * K - k0) * 2u : 0u);
     ++g_stage;
+    if constexpr (WB) {
+      const __amdgpu_buffer_rsrc_t rh =
+          window32(Wh + int64_t(k0) * d_in + i0,
+                   rows_k > 0 ? uint32_t(rows_k * d_in - i0) * 2u : 0u);
 #pragma unroll
-    for (int j = 0; j < NA; ++j)
-      wr[j] = __builtin_bit_cast(
-          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                       rw, (int)a_voff, (int)(RPI_A * (NA * wave + j) * d_in * 4), 0));
+      for (int j = 0; j < NQA; ++j) {
+        const int q = NQA * wave + j;
+        load16_to_lds(rh, slot + q * 512, h_voff[j], q * RPQ * d_in * 2);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rw =
+          window32(W + int64_t(k0) * d_in + i0,
+                   rows_k > 0 ? uint32_t(rows_k * d_in - i0) * 4u : 0u);
+#pragma unroll
+      for (int j = 0; j < NA; ++j)
+        wr[j] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rw, (int)a_voff, (int)(RPI_A * (NA * wave + j) * d_in * 4), 0));
+    }
     const uint32_t bv = k0 + 8 * b_chunk < K ? b_voff : kOOB;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -102,9 +135,12 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
     }
   };
   auto convert_write = [&](uint16_t* slot, const f32x4_t (&wr)[NA]) {
-    char* base = reinterpret_cast<char*>(slot);
+    if constexpr (!WB) {
+      char* base = reinterpret_cast<char*>(slot);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) *reinterpret_cast<u32x2_t*>(base + a_lds[j]) = pack_bf16x4(wr[j]);
+      for (int j = 0; j < NA; ++j)
+        *reinterpret_cast<u32x2_t*>(base + a_lds[j]) = pack_bf16x4(wr[j]);
+    }
   };
 
   // Operand addresses. A: the transpose-read pattern of the weight-gradient
@@ -168,9 +204,9 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
       if (i < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // VMEM read
     }
   };
-  // After this wave's loads of stage s + 2 (NA + NB) are issued, the stage
+  // After this wave's loads of stage s + 2 (NAL + NB) are issued, the stage
   // s + 1 loads are complete when at most that many remain.
-  constexpr int kWait = waitcnt_imm(NA + NB, 0);
+  constexpr int kWait = waitcnt_imm(NAL + NB, 0);
 #define FORGE_DGRAD_BARRIER(IMM)              \
   do {                                        \
     __builtin_amdgcn_sched_barrier(0);        \
@@ -189,7 +225,7 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
     issue(fut, w_fut);
     read_frags(1, cur, 1);
     mfmas(0);
-    interleave(NA + NB);
+    interleave(NAL + NB);
     __builtin_amdgcn_sched_barrier(0);
     convert_write(nxt, w_nxt);
     FORGE_DGRAD_BARRIER(kWait);
@@ -222,14 +258,15 @@ __device__ __forceinline__ void dgrad_tile(const WgradArgs& a, const uint16_t* _
                    reinterpret_cast<float*>(ep));
 }
 
-// Grid launch, one workgroup per dX^T tile in the XCD-aware walk.
-template <class C, int EPI>
+// Grid launch, one workgroup per dX^T tile in the XCD-aware walk. W: float32
+// weights, or with WB their bf16 copy.
+template <class C, int EPI, bool WB>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
-void dgrad_kernel(WgradArgs a, const float* W, int K) {
+void dgrad_kernel(WgradArgs a, const void* W, int K) {
   FORGE_DECLARE_SLOTS(C::STAGE);
   int e, tm, tn;
   map_tile(blockIdx.x, a.num_tiles, a.tiles_m, a.tiles_n, a.group_m, e, tm, tn);
-  dgrad_tile<C, EPI>(a, a.dY, W, K, tm, tn, ring);
+  dgrad_tile<C, EPI, WB>(a, a.dY, W, K, tm, tn, ring);
 }
 
 }  // namespace forge

@@ -52,6 +52,43 @@ forge_status with_adamw_epi(const forge_adamw_params& p, Args&&... args) {
   return p.eps > 0.0 ? F<BASE>::run(args...) : F<BASE | EPI_EXACT_SQRT>::run(args...);
 }
 
+// Dense weight-gradient launches: a grid of tiles of configuration C, or the
+// persistent schedule (full 256x256 and half 256x128 tiles).
+template <class C, int EPI>
+forge_status launch_dense_t(WgradArgs a, hipStream_t s) {
+  set_grid<C>(a, 1);
+  hipLaunchKernelGGL((wgrad_dense_kernel<C, EPI>), dim3(a.num_tiles), dim3(C::THREADS), 0, s, a);
+  return launch_status();
+}
+
+template <int EPI>
+forge_status launch_persistent(WgradArgs a, hipStream_t s) {
+  set_grid<Cfg256x256>(a, 1);
+  const int grid = persistent_grid();
+  if (grid <= 0) return launch_dense_t<Cfg256x256, EPI>(a, s);
+  hipLaunchKernelGGL((wgrad_persistent_kernel<Cfg256x256, Cfg256x128, EPI>), dim3(grid),
+                     dim3(Cfg256x256::THREADS), 0, s, a);
+  return launch_status();
+}
+
+template <int EPI>
+forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
+  switch (tile) {
+    case FORGE_TILE_128x128: return launch_dense_t<Cfg128x128, EPI>(a, s);
+    case FORGE_TILE_256x128: return launch_dense_t<Cfg256x128, EPI>(a, s);
+    case FORGE_TILE_256x256: return launch_dense_t<Cfg256x256, EPI>(a, s);
+    case FORGE_TILE_PERSISTENT: return launch_persistent<EPI>(a, s);
+    default: return FORGE_ERR_TILE;
+  }
+}
+
+template <int EPI>
+struct DenseLaunch {
+  static forge_status run(const WgradArgs& a, forge_tile tile, hipStream_t s) {
+    return launch_dense<EPI>(a, tile, s);
+  }
+};
+
 // The fused weight-gradient launches of forge.hip, for the linear-backward
 // calls (one instantiation of each kernel in the library).
 forge_status launch_wgrad_adamw(const WgradArgs& a, const forge_adamw_params& p, forge_tile tile,

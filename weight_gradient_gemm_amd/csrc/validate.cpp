@@ -291,8 +291,12 @@ forge_status validate_wgrad_adamw_fp8(const void* X8, forge_dtype x_fmt, double 
   return check_tile(tile);
 }
 
-forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forge_dtype dX_dtype,
-                            int64_t T, int64_t d_in, int64_t d_out, forge_tile tile) {
+namespace {
+
+// dX = dY W with W of w_bytes bytes per element (float32 or its bf16 copy).
+forge_status check_dgrad(const void* dY, const void* W, int w_bytes, const void* dX,
+                         forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
+                         forge_tile tile) {
   const int xb = dtype_bytes(dX_dtype);
   if (xb == 0) return FORGE_ERR_DTYPE;
   if (T < 0 || d_in < 0 || d_out < 0) return FORGE_ERR_SHAPE;
@@ -305,12 +309,10 @@ forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forg
   if (d_out > 0 && (!aligned16(dY) || !aligned16(W))) return FORGE_ERR_ALIGN;
   const Span sx{dX, uint64_t(T) * uint64_t(d_in) * uint64_t(xb)};
   const Span sy{dY, uint64_t(T) * uint64_t(d_out) * 2u};
-  const Span sw{W, uint64_t(d_out) * uint64_t(d_in) * 4u};
+  const Span sw{W, uint64_t(d_out) * uint64_t(d_in) * uint64_t(w_bytes)};
   if (spans_overlap(sx, sy) || spans_overlap(sx, sw)) return FORGE_ERR_ALIAS;
   return check_tile(tile);
 }
-
-namespace {
 
 // The linear-backward calls: dX must also stay clear of X and the state
 // the fused step writes.
@@ -326,6 +328,17 @@ forge_status check_dx_clear(const void* dX, forge_dtype dX_dtype, int64_t T, int
 }
 
 }  // namespace
+
+forge_status validate_dgrad(const void* dY, const float* W, const void* dX, forge_dtype dX_dtype,
+                            int64_t T, int64_t d_in, int64_t d_out, forge_tile tile) {
+  return check_dgrad(dY, W, 4, dX, dX_dtype, T, d_in, d_out, tile);
+}
+
+forge_status validate_dgrad_bf16w(const void* dY, const void* Wb, const void* dX,
+                                  forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
+                                  forge_tile tile) {
+  return check_dgrad(dY, Wb, 2, dX, dX_dtype, T, d_in, d_out, tile);
+}
 
 forge_status validate_linear_backward_adamw(const void* X, const void* dY, const float* W,
                                             const float* m, const float* v, const void* dX,
@@ -348,6 +361,43 @@ forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const 
     return s;
   const void* state[1] = {mom};
   return check_dx_clear(dX, dX_dtype, T, d_in, d_out, X, state, 1);
+}
+
+// The bf16-copy calls: Wb is written by the fused step, so it is checked as
+// one more output (disjoint from W, the state, X and dY); dX is read from Wb
+// and must stay clear of W as well.
+forge_status validate_linear_backward_adamw_bf16w(const void* X, const void* dY, const float* W,
+                                                  const float* m, const float* v, const void* Wb,
+                                                  const void* dX, forge_dtype dX_dtype, int64_t T,
+                                                  int64_t d_in, int64_t d_out,
+                                                  const forge_adamw_params* p, forge_tile tile) {
+  const void* outs[4] = {W, m, v, Wb};
+  const int bytes[4] = {4, 4, 4, 2};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 4, T, d_in, d_out)) return s;
+  if (forge_status s = check_adamw_params(p)) return s;
+  if (forge_status s = check_tile(tile)) return s;
+  if (forge_status s = check_dgrad(dY, Wb, 2, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
+    return s;
+  const void* state[3] = {W, m, v};
+  return check_dx_clear(dX, dX_dtype, T, d_in, d_out, X, state, 3);
+}
+
+forge_status validate_linear_backward_sgdm_bf16w(const void* X, const void* dY, const float* W,
+                                                 const float* mom, const void* Wb, const void* dX,
+                                                 forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                                 int64_t d_out, const forge_sgdm_params* p,
+                                                 forge_tile tile) {
+  const void* outs[3] = {W, mom, Wb};
+  const int bytes[3] = {4, 4, 2};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 3, T, d_in, d_out)) return s;
+  if (forge_status s = check_sgdm_params(p)) return s;
+  if (forge_status s = check_tile(tile)) return s;
+  if (forge_status s = check_dgrad(dY, Wb, 2, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
+    return s;
+  const void* state[2] = {W, mom};
+  return check_dx_clear(dX, dX_dtype, T, d_in, d_out, X, state, 2);
 }
 
 }  // namespace forge

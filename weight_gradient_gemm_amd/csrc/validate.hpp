@@ -81,6 +81,19 @@ forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const 
                                            const float* mom, const void* dX, forge_dtype dX_dtype,
                                            int64_t T, int64_t d_in, int64_t d_out,
                                            const forge_sgdm_params* p, forge_tile tile);
+forge_status validate_dgrad_bf16w(const void* dY, const void* Wb, const void* dX,
+                                  forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
+                                  forge_tile tile);
+forge_status validate_linear_backward_adamw_bf16w(const void* X, const void* dY, const float* W,
+                                                  const float* m, const float* v, const void* Wb,
+                                                  const void* dX, forge_dtype dX_dtype, int64_t T,
+                                                  int64_t d_in, int64_t d_out,
+                                                  const forge_adamw_params* p, forge_tile tile);
+forge_status validate_linear_backward_sgdm_bf16w(const void* X, const void* dY, const float* W,
+                                                 const float* mom, const void* Wb, const void* dX,
+                                                 forge_dtype dX_dtype, int64_t T, int64_t d_in,
+                                                 int64_t d_out, const forge_sgdm_params* p,
+                                                 forge_tile tile);
 forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
                                     const int64_t* offsets, int32_t E, const float* W,
                                     const float* m, const float* v, int64_t d_in, int64_t d_out,

@@ -50,6 +50,7 @@ enum Epi : int {
   EPI_BF16_STATE = 8,   // AdamW m and v stored as bf16 (W stays float32)
   EPI_BF16_OUT = 16,    // gradient store rounded to bf16
   EPI_SCALE = 32,       // the accumulator times WgradArgs::gscale (scaled fp8 inputs)
+  EPI_WB_OUT = 64,      // AdamW / SGD: the updated W also stored as bf16 into WgradArgs::Wb
 };
 
 __host__ __device__ constexpr int epi_op(int epi) { return epi & 3; }
@@ -79,6 +80,7 @@ struct WgradArgs {
   AdamWConsts adam;
   SgdmConsts sgd;
   float gscale;        // EPI_SCALE: factor applied to the accumulator once
+  uint16_t* Wb;        // EPI_WB_OUT: [d_out, d_in] bf16 copy of the updated W (dense only)
 };
 
 struct GroupTable {
@@ -280,9 +282,11 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   constexpr int D = 2;                       // units in flight
   constexpr int OP = epi_op(EPI);
   constexpr int NS = OP == EPI_ADAMW ? 3 : (OP == EPI_SGDM ? 2 : 0);   // state arrays read
-  // Bytes per element of W (or the gradient), S1 and S2.
+  // Bytes per element of W (or the gradient), S1, S2 and the bf16 copy of W.
   constexpr int ESW = epi_w_bytes(EPI), ESS = epi_state_bytes(EPI);
-  constexpr int ES[3] = {ESW, ESS, ESS};
+  constexpr int ES[4] = {ESW, ESS, ESS, 2};
+  constexpr bool WB = (EPI & EPI_WB_OUT) != 0;
+  static_assert(!WB || (OP != EPI_GRAD && ESW == 4), "the bf16 copy is of an updated W");
   static_assert(NI % B == 0, "epilogue units must tile a block");
   static_assert(32 * LD * 4 <= C::STAGE * 2, "a wave's epilogue staging exceeds a slot");
 
@@ -292,8 +296,8 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
   const int iw0 = i0 + wm * WM;
   const bool lane_ok = iw0 + c_lane < d_in;
   const uint32_t elem = uint32_t(r_lane * d_in + c_lane);   // lane's first element in a block
-  char* const arr[3] = {reinterpret_cast<char*>(W), reinterpret_cast<char*>(S1),
-                        reinterpret_cast<char*>(S2)};
+  char* const arr[4] = {reinterpret_cast<char*>(W), reinterpret_cast<char*>(S1),
+                        reinterpret_cast<char*>(S2), reinterpret_cast<char*>(a.Wb)};
   // Array k: the lane's byte offset, the bytes between row instructions, and
   // the window from the wave's first column of block n's first row.
   auto voff = [&](int k) { return lane_ok ? elem * uint32_t(ES[k]) : kOOB; };
@@ -354,6 +358,7 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
         store4<ESW>(rw, voff(0), (j0 + j) * inst_bytes(0), s);
         store4<ESS>(r1, voff(1), (j0 + j) * inst_bytes(1), st[u % D][j][1]);
         store4<ESS>(r2, voff(2), (j0 + j) * inst_bytes(2), st[u % D][j][2]);
+        if constexpr (WB) store4<2>(block_window(3, n), voff(3), (j0 + j) * inst_bytes(3), s);
       }
     } else {
       const __amdgpu_buffer_rsrc_t r1 = block_window(1, n);
@@ -362,6 +367,8 @@ __device__ __forceinline__ void epilogue(const WgradArgs& a, f32x16_t (&acc)[C::
         sgdm_vec4(g[j], st[u % D][j][0], st[u % D][j][1], a.sgd);
         store4<ESW>(rw, voff(0), (j0 + j) * inst_bytes(0), st[u % D][j][0]);
         store4<ESS>(r1, voff(1), (j0 + j) * inst_bytes(1), st[u % D][j][1]);
+        if constexpr (WB)
+          store4<2>(block_window(3, n), voff(3), (j0 + j) * inst_bytes(3), st[u % D][j][0]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -387,6 +394,7 @@ __device__ __forceinline__ void epilogue_wide(const WgradArgs& a, f32x16_t (&acc
   constexpr int U = TN * UPB;
   constexpr int D = 2;                       // units in flight
   static_assert(is_adamw(EPI) && (EPI & EPI_BF16_STATE), "bf16-state AdamW only");
+  static_assert((EPI & EPI_WB_OUT) == 0, "no bf16 weight copy with bf16 state");
   static_assert(NI % B == 0, "epilogue units must tile a block");
   static_assert(32 * LD * 4 <= C::STAGE * 2, "a wave's epilogue staging exceeds a slot");
 
@@ -692,6 +700,7 @@ void wgrad_dense_kernel(WgradArgs a) {
 template <class C, int EPI>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
+  static_assert((EPI & EPI_WB_OUT) == 0, "the bf16 weight copy is a dense-call output");
   FORGE_DECLARE_SLOTS(C::STAGE);
   const int per_expert = a.tiles_m * a.tiles_n;
   const int slot = blockIdx.x / per_expert;
