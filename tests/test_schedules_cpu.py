@@ -20,8 +20,10 @@ PROGRAM = textwrap.dedent(r"""
     #include "wgrad_kernels.hpp"
     using namespace forge;
 
+    // Every even worker count per XCD a device can give (the launch uses
+    // whole pairs per XCD, up to 32 compute units per XCD).
     static int check_persistent() {
-      const int nw = 32;
+      for (int nw = 2; nw <= 32; nw += 2)
       for (int R = 1; R <= 3000; ++R) {
         for (int phase = 0; phase < 2; ++phase) {
           if (phase && forge::schedule_phase(1, R, nw) == 0) continue;
@@ -35,7 +37,7 @@ PROGRAM = textwrap.dedent(r"""
             }
           }
           for (int i = 0; i < 2 * R; ++i)
-            if (cover[i] != 1) { printf("persistent: R=%d phase %d half-tile %d covered %d times\n", R, phase, i, cover[i]); return 1; }
+            if (cover[i] != 1) { printf("persistent: nw=%d R=%d phase %d half-tile %d covered %d times\n", nw, R, phase, i, cover[i]); return 1; }
         }
       }
       return 0;
