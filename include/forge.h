@@ -19,10 +19,11 @@
  * transposed-lhs matmul, with its reduction kept whole per output tile).
  *
  * Conventions shared by every entry point:
- *   - Every pointer named X, dY, W, m, v, mom, grad is a DEVICE pointer owned
- *     by the caller; the library allocates nothing and keeps no state between
- *     calls except a per-device architecture check. bfloat16 arrays are passed
- *     as raw 16-bit storage. All arrays are dense row-major.
+ *   - Every pointer named X, dY, W, m, v, mom, grad, dX, Wb (and their fp8 and
+ *     bf16 forms) is a DEVICE pointer owned by the caller; the library
+ *     allocates nothing and keeps no state between calls except a per-device
+ *     architecture check. bfloat16 arrays are passed as raw 16-bit storage.
+ *     All arrays are dense row-major.
  *   - W, m, v, mom are float32 and updated in place. X and dY are read only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous and stream-ordered; FORGE_OK means "validated and
