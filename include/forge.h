@@ -314,6 +314,10 @@ FORGE_API forge_status forge_linear_backward_sgdm(const void* X, const void* dY,
  * forge_linear_backward_adamw (_sgdm), and Wb holds bf16(W) again on return:
  * the caller rounds W once, before the first step. Contract otherwise as
  * those calls.
+ * forge_wgrad_adamw_bf16w / forge_wgrad_sgdm_bf16w: the fused step alone
+ * (no input gradient, e.g. for a layer whose input needs none), storing the
+ * updated W rounded to bf16 into Wb; W and its state get the bits of
+ * forge_wgrad_adamw (_sgdm). Contract otherwise as those calls.
  */
 FORGE_API forge_status forge_dgrad_bf16w(const void* dY, const void* Wb, void* dX,
                                forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
@@ -328,6 +332,13 @@ FORGE_API forge_status forge_linear_backward_sgdm_bf16w(const void* X, const voi
                                               forge_dtype dX_dtype, int64_t T, int64_t d_in,
                                               int64_t d_out, const forge_sgdm_params* p,
                                               forge_tile tile, void* stream);
+FORGE_API forge_status forge_wgrad_adamw_bf16w(const void* X, const void* dY, float* W, float* m,
+                                     float* v, void* Wb, int64_t T, int64_t d_in, int64_t d_out,
+                                     const forge_adamw_params* p, forge_tile tile,
+                                     void* stream);
+FORGE_API forge_status forge_wgrad_sgdm_bf16w(const void* X, const void* dY, float* W, float* mom,
+                                    void* Wb, int64_t T, int64_t d_in, int64_t d_out,
+                                    const forge_sgdm_params* p, forge_tile tile, void* stream);
 
 /*
  * Weight gradient from fp8 inputs. FORGE assessment, "Math verified, not

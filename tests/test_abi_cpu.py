@@ -41,8 +41,8 @@ def test_every_declared_symbol_is_exported(lib, root):
                             "forge_linear_backward_sgdm", "forge_linear_backward_sgdm_bf16w",
                             "forge_sgdm", "forge_status_string",
                             "forge_wgrad", "forge_wgrad_adamw", "forge_wgrad_adamw_bf16state",
-                            "forge_wgrad_adamw_fp8", "forge_wgrad_bf16", "forge_wgrad_fp8",
-                            "forge_wgrad_sgdm"])
+                            "forge_wgrad_adamw_bf16w", "forge_wgrad_adamw_fp8", "forge_wgrad_bf16", "forge_wgrad_fp8",
+                            "forge_wgrad_sgdm", "forge_wgrad_sgdm_bf16w"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path], check=True,
@@ -140,6 +140,10 @@ def test_no_gpu_means_device_error(lib):
                                                  32, ctypes.byref(adam()), 0, None) == 8
     assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, D, 0, 64, 64, 32,
                                                 ctypes.byref(sgd()), 0, None) == 8
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, WB_ADDR, 64, 64, 32,
+                                       ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_wgrad_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, 64, 64, 32,
+                                      ctypes.byref(sgd()), 0, None) == 8
 
 
 def test_sgdm_and_unfused_reject(lib):
@@ -265,6 +269,24 @@ def test_bf16_weight_copy_calls_reject(lib):
     # nothing to write: no device needed
     assert lib.forge_linear_backward_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, D, F32, T, 0,
                                                 d_out, ctypes.byref(sgd()), 0, None) == 0
+    # the fused steps alone
+    p = adam()
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, NULL, T, d_in, d_out,
+                                       ctypes.byref(p), 0, None) == 1
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, WB_ADDR + 8, T, d_in, d_out,
+                                       ctypes.byref(p), 0, None) == 3
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, C + 16, T, d_in, d_out,
+                                       ctypes.byref(p), 0, None) == 4
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, WB_ADDR, T, d_in, d_out,
+                                       ctypes.byref(adam(max_grad_norm=2.0)), 0, None) == 6
+    assert lib.forge_wgrad_adamw_bf16w(X_ADDR, Y_ADDR, A, B, C, WB_ADDR, T, d_in, d_out,
+                                       ctypes.byref(p), 8, None) == 7
+    assert lib.forge_wgrad_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, Y_ADDR + 32, T, d_in, d_out,
+                                      ctypes.byref(sgd()), 0, None) == 4
+    assert lib.forge_wgrad_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, T, d_in, d_out,
+                                      ctypes.byref(sgd(lr=-1.0)), 0, None) == 5
+    assert lib.forge_wgrad_sgdm_bf16w(X_ADDR, Y_ADDR, A, B, WB_ADDR, T, 0, d_out,
+                                      ctypes.byref(sgd()), 0, None) == 0
 
 
 def test_fp8_rejects(lib):

@@ -271,3 +271,43 @@ def test_linear_backward_bf16w_zero_tokens(wg):
     assert bits_equal(host(m), np.float32(0.9) * m0)
     assert _copy_is_rounded(Wb, W)
     assert not bits_equal(host(W), W0)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_fused_steps_refresh_the_bf16_copy(wg, tile):
+    """The fused steps alone with the copy refresh: W and the state judged
+    against the oracle and bitwise those of the plain fused calls; the copy
+    the oracle's bf16 rounding of the new W."""
+    case = CASES[0]
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v, Wb = f32_dev(W0), f32_dev(m0), f32_dev(v0), _wb_dev(np.zeros_like(W0))
+    W2, m2, v2 = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp)
+    for t in (1, 2):
+        Xb, dYb = synth.dense_inputs(case, 30 + t)
+        X, dY = bf16_dev(Xb), bf16_dev(dYb)
+        log(f"[{case.name}] fused AdamW refreshing the bf16 copy, tile {tile}, step {t}")
+        W_prev = host(W)
+        wg.forge_wgrad_adamw_bf16w(X, dY, W, m, v, Wb, step=t, tile=tile, **hp)
+        wg.forge_wgrad_adamw(X, dY, W2, m2, v2, step=t, tile=tile, **hp)
+        _sync()
+        rep = par.step(t, oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W_prev, host(W),
+                       host(m), host(v))
+        assert rep.passed, str(rep)
+        assert _copy_is_rounded(Wb, W)
+        assert bits_equal(host(W), host(W2)) and bits_equal(host(m), host(m2))
+        assert bits_equal(host(v), host(v2))
+    hs = dict(lr=case.lr, momentum=case.momentum, weight_decay=0.01)
+    W, b, Wb = f32_dev(W0), f32_dev(np.zeros_like(W0)), _wb_dev(np.zeros_like(W0))
+    W2, b2 = f32_dev(W0), f32_dev(np.zeros_like(W0))
+    spar = SgdmParity(W0, np.zeros_like(W0), hs)
+    Xb, dYb = synth.dense_inputs(case, 40)
+    log(f"[{case.name}] fused SGD-momentum refreshing the bf16 copy, tile {tile}")
+    wg.forge_wgrad_sgdm_bf16w(bf16_dev(Xb), bf16_dev(dYb), W, b, Wb, tile=tile, **hs)
+    wg.forge_wgrad_sgdm(bf16_dev(Xb), bf16_dev(dYb), W2, b2, tile=tile, **hs)
+    _sync()
+    rep = spar.step(oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W0, host(W), host(b))
+    assert rep.passed, str(rep)
+    assert _copy_is_rounded(Wb, W)
+    assert bits_equal(host(W), host(W2)) and bits_equal(host(b), host(b2))

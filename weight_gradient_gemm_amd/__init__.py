@@ -32,10 +32,12 @@ from ._lib import (  # noqa: F401
     forge_wgrad,
     forge_wgrad_adamw,
     forge_wgrad_adamw_bf16state,
+    forge_wgrad_adamw_bf16w,
     forge_wgrad_adamw_fp8,
     forge_wgrad_bf16,
     forge_wgrad_fp8,
     forge_wgrad_sgdm,
+    forge_wgrad_sgdm_bf16w,
     library,
     library_path,
 )

@@ -92,6 +92,10 @@ def library() -> ctypes.CDLL:
         lib.forge_linear_backward_sgdm_bf16w.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, ctypes.POINTER(SgdmParams),
             _i32, _vp]
+        lib.forge_wgrad_adamw_bf16w.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                                ctypes.POINTER(AdamWParams), _i32, _vp]
+        lib.forge_wgrad_sgdm_bf16w.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                               ctypes.POINTER(SgdmParams), _i32, _vp]
         _d = ctypes.c_double
         lib.forge_wgrad_fp8.argtypes = [_vp, _i32, _d, _vp, _i32, _d, _vp, _i64, _i64, _i64,
                                         _i32, _vp]
@@ -104,7 +108,8 @@ def library() -> ctypes.CDLL:
                      "forge_wgrad_adamw_bf16state", "forge_adamw_mixed", "forge_dgrad",
                      "forge_linear_backward_adamw", "forge_linear_backward_sgdm",
                      "forge_wgrad_fp8", "forge_wgrad_adamw_fp8", "forge_dgrad_bf16w",
-                     "forge_linear_backward_adamw_bf16w", "forge_linear_backward_sgdm_bf16w"):
+                     "forge_linear_backward_adamw_bf16w", "forge_linear_backward_sgdm_bf16w",
+                     "forge_wgrad_adamw_bf16w", "forge_wgrad_sgdm_bf16w"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -433,6 +438,38 @@ def forge_linear_backward_sgdm_bf16w(X, dY, W, mom, Wb, dX, *, lr=1e-3, momentum
     _check(library().forge_linear_backward_sgdm_bf16w(
         _ptr(X), _ptr(dY), _ptr(W), _ptr(mom), _ptr(Wb), _ptr(dX), code, T, d_in, d_out,
         ctypes.byref(p), int(tile), _stream(stream)), "forge_linear_backward_sgdm_bf16w")
+
+
+def _wb_like(Wb, d_out, d_in):
+    torch = _torch()
+    _want(Wb, torch.bfloat16, "Wb")
+    if tuple(Wb.shape) != (d_out, d_in):
+        raise ValueError(f"Wb must have shape {(d_out, d_in)}, got {tuple(Wb.shape)}")
+
+
+def forge_wgrad_adamw_bf16w(X, dY, W, m, v, Wb, *, step, lr=1e-3, beta1=0.9, beta2=0.999,
+                            eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                            tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """The fused AdamW step of forge_wgrad_adamw, also storing bf16(W) into Wb."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("m", m), ("v", v)), d_out, d_in)
+    _wb_like(Wb, d_out, d_in)
+    p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
+    _check(library().forge_wgrad_adamw_bf16w(_ptr(X), _ptr(dY), _ptr(W), _ptr(m), _ptr(v),
+                                             _ptr(Wb), T, d_in, d_out, ctypes.byref(p), int(tile),
+                                             _stream(stream)), "forge_wgrad_adamw_bf16w")
+
+
+def forge_wgrad_sgdm_bf16w(X, dY, W, mom, Wb, *, lr=1e-3, momentum=0.9, weight_decay=0.0,
+                           max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """The fused SGD-momentum step of forge_wgrad_sgdm, also storing bf16(W) into Wb."""
+    T, d_in, d_out = _xdy(X, dY)
+    _state_like(W, (("mom", mom),), d_out, d_in)
+    _wb_like(Wb, d_out, d_in)
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_wgrad_sgdm_bf16w(_ptr(X), _ptr(dY), _ptr(W), _ptr(mom), _ptr(Wb), T,
+                                            d_in, d_out, ctypes.byref(p), int(tile),
+                                            _stream(stream)), "forge_wgrad_sgdm_bf16w")
 
 
 _FP8 = {"e4m3": FORGE_FP8_E4M3, "e5m2": FORGE_FP8_E5M2}

@@ -1,7 +1,8 @@
 // Input-gradient entry points of the forge C ABI: dX = dY W_b on its own,
 // and the linear-layer backward that issues it before the fused optimizer
 // step on the same stream; each from the float32 weight or from a bf16 copy
-// of it (which the fused step then refreshes).
+// of it (which the fused step then refreshes). Also the fused steps that
+// refresh such a copy without an input gradient.
 #include "dgrad_kernels.hpp"
 #include "host.hpp"
 #include "validate.hpp"
@@ -175,6 +176,40 @@ FORGE_API forge_status forge_linear_backward_sgdm_bf16w(const void* X, const voi
   a.Wb = static_cast<uint16_t*>(Wb);
   return linear_backward<true>(dY, Wb, dX, dX_dtype, T, d_in, d_out, a, tile, stream,
                                launch_wgrad_sgdm_wb);
+}
+
+FORGE_API forge_status forge_wgrad_adamw_bf16w(const void* X, const void* dY, float* W, float* m,
+                                               float* v, void* Wb, int64_t T, int64_t d_in,
+                                               int64_t d_out, const forge_adamw_params* p,
+                                               forge_tile tile, void* stream) {
+  if (forge_status s = validate_wgrad_adamw_bf16w(X, dY, W, m, v, Wb, T, d_in, d_out, p, tile))
+    return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, W, m, v, T, d_in, d_out);
+  a.adam = make_adamw(*p);
+  a.Wb = static_cast<uint16_t*>(Wb);
+  return launch_wgrad_adamw_wb(a, *p, tile, static_cast<hipStream_t>(stream));
+}
+
+FORGE_API forge_status forge_wgrad_sgdm_bf16w(const void* X, const void* dY, float* W, float* mom,
+                                              void* Wb, int64_t T, int64_t d_in, int64_t d_out,
+                                              const forge_sgdm_params* p, forge_tile tile,
+                                              void* stream) {
+  if (forge_status s = validate_wgrad_sgdm_bf16w(X, dY, W, mom, Wb, T, d_in, d_out, p, tile))
+    return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  tile = resolve_tile(tile, d_in, d_out, 1);
+  if (!grid_fits(d_in, d_out, tile, 1)) return FORGE_ERR_SHAPE;
+  (void)hipGetLastError();
+  WgradArgs a = base_args(X, dY, W, mom, nullptr, T, d_in, d_out);
+  a.sgd = make_sgdm(*p);
+  a.Wb = static_cast<uint16_t*>(Wb);
+  return launch_wgrad_sgdm_wb(a, tile, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -364,19 +364,39 @@ forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const 
 }
 
 // The bf16-copy calls: Wb is written by the fused step, so it is checked as
-// one more output (disjoint from W, the state, X and dY); dX is read from Wb
-// and must stay clear of W as well.
-forge_status validate_linear_backward_adamw_bf16w(const void* X, const void* dY, const float* W,
-                                                  const float* m, const float* v, const void* Wb,
-                                                  const void* dX, forge_dtype dX_dtype, int64_t T,
-                                                  int64_t d_in, int64_t d_out,
-                                                  const forge_adamw_params* p, forge_tile tile) {
+// one more output (disjoint from W, the state, X and dY); in the
+// linear-backward calls dX is read from Wb and must stay clear of W as well.
+forge_status validate_wgrad_adamw_bf16w(const void* X, const void* dY, const float* W,
+                                        const float* m, const float* v, const void* Wb,
+                                        int64_t T, int64_t d_in, int64_t d_out,
+                                        const forge_adamw_params* p, forge_tile tile) {
   const void* outs[4] = {W, m, v, Wb};
   const int bytes[4] = {4, 4, 4, 2};
   if (!p) return FORGE_ERR_NULL;
   if (forge_status s = check_dense_sized(X, dY, outs, bytes, 4, T, d_in, d_out)) return s;
   if (forge_status s = check_adamw_params(p)) return s;
-  if (forge_status s = check_tile(tile)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_wgrad_sgdm_bf16w(const void* X, const void* dY, const float* W,
+                                       const float* mom, const void* Wb, int64_t T, int64_t d_in,
+                                       int64_t d_out, const forge_sgdm_params* p,
+                                       forge_tile tile) {
+  const void* outs[3] = {W, mom, Wb};
+  const int bytes[3] = {4, 4, 2};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 3, T, d_in, d_out)) return s;
+  if (forge_status s = check_sgdm_params(p)) return s;
+  return check_tile(tile);
+}
+
+forge_status validate_linear_backward_adamw_bf16w(const void* X, const void* dY, const float* W,
+                                                  const float* m, const float* v, const void* Wb,
+                                                  const void* dX, forge_dtype dX_dtype, int64_t T,
+                                                  int64_t d_in, int64_t d_out,
+                                                  const forge_adamw_params* p, forge_tile tile) {
+  if (forge_status s = validate_wgrad_adamw_bf16w(X, dY, W, m, v, Wb, T, d_in, d_out, p, tile))
+    return s;
   if (forge_status s = check_dgrad(dY, Wb, 2, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
     return s;
   const void* state[3] = {W, m, v};
@@ -388,12 +408,8 @@ forge_status validate_linear_backward_sgdm_bf16w(const void* X, const void* dY, 
                                                  forge_dtype dX_dtype, int64_t T, int64_t d_in,
                                                  int64_t d_out, const forge_sgdm_params* p,
                                                  forge_tile tile) {
-  const void* outs[3] = {W, mom, Wb};
-  const int bytes[3] = {4, 4, 2};
-  if (!p) return FORGE_ERR_NULL;
-  if (forge_status s = check_dense_sized(X, dY, outs, bytes, 3, T, d_in, d_out)) return s;
-  if (forge_status s = check_sgdm_params(p)) return s;
-  if (forge_status s = check_tile(tile)) return s;
+  if (forge_status s = validate_wgrad_sgdm_bf16w(X, dY, W, mom, Wb, T, d_in, d_out, p, tile))
+    return s;
   if (forge_status s = check_dgrad(dY, Wb, 2, dX, dX_dtype, T, d_in, d_out, FORGE_TILE_DEFAULT))
     return s;
   const void* state[2] = {W, mom};

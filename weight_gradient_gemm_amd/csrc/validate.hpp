@@ -84,6 +84,14 @@ forge_status validate_linear_backward_sgdm(const void* X, const void* dY, const 
 forge_status validate_dgrad_bf16w(const void* dY, const void* Wb, const void* dX,
                                   forge_dtype dX_dtype, int64_t T, int64_t d_in, int64_t d_out,
                                   forge_tile tile);
+forge_status validate_wgrad_adamw_bf16w(const void* X, const void* dY, const float* W,
+                                        const float* m, const float* v, const void* Wb,
+                                        int64_t T, int64_t d_in, int64_t d_out,
+                                        const forge_adamw_params* p, forge_tile tile);
+forge_status validate_wgrad_sgdm_bf16w(const void* X, const void* dY, const float* W,
+                                       const float* mom, const void* Wb, int64_t T, int64_t d_in,
+                                       int64_t d_out, const forge_sgdm_params* p,
+                                       forge_tile tile);
 forge_status validate_linear_backward_adamw_bf16w(const void* X, const void* dY, const float* W,
                                                   const float* m, const float* v, const void* Wb,
                                                   const void* dX, forge_dtype dX_dtype, int64_t T,
