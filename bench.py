@@ -80,6 +80,35 @@ def read_traffic(workload: str, sha: str):
     return float(m_b.group(1))
 
 
+def read_counters(workload: str, sha: str, n_param: int):
+    """The rest of the committed counter summaries for the fused kernel, where
+    they were taken on the current kernel sources: HBM bytes written per
+    parameter (the optimizer state only, if the gradient never reaches HBM),
+    the unfused pair's bytes per step, and the matrix cores' busy fraction."""
+    out = {}
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    if os.path.exists(path):
+        with open(path) as f:
+            text = f.read()
+        m_sha = re.search(r"^kernel_source_sha:\s*(\w+)", text, re.M)
+        m_w = re.search(r"^fused_write_bytes:\s*([0-9.eE+]+)", text, re.M)
+        m_u = re.search(r"^unfused_pair_hbm_bytes_per_step:\s*([0-9.eE+]+)", text, re.M)
+        if m_sha and m_sha.group(1) == sha:
+            if m_w:
+                out["fused_write_bytes_per_param"] = round(float(m_w.group(1)) / n_param, 3)
+            if m_u:
+                out["unfused_pair_hbm_bytes"] = float(m_u.group(1))
+    path = os.path.join(ROOT, "profiles", f"pmc_mfma_{workload}.txt")
+    if os.path.exists(path):
+        with open(path) as f:
+            text = f.read()
+        m_sha = re.search(r"^kernel_source_sha:\s*(\w+)", text, re.M)
+        m_b = re.search(r"^\| fused [^|]*\|\s*([0-9.]+)\s*\|", text, re.M)
+        if m_sha and m_sha.group(1) == sha and m_b:
+            out["mfma_busy_fraction"] = float(m_b.group(1))
+    return out or None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +360,7 @@ def main():
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     sha = kernel_source_sha()
     traffic = read_traffic(args.workload, sha)
+    counters = read_counters(args.workload, sha, n_param)
 
     cpu = None
     if not args.no_cpu:
@@ -406,6 +436,7 @@ def main():
         "precision_variants": variants,
         "backward": backward,
         "kernel_source_sha": sha,
+        "counters": counters,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
