@@ -103,7 +103,9 @@ def read_counters(workload: str, sha: str, n_param: int):
         with open(path) as f:
             text = f.read()
         m_sha = re.search(r"^kernel_source_sha:\s*(\w+)", text, re.M)
-        m_b = re.search(r"^\| fused [^|]*\|\s*([0-9.]+)\s*\|", text, re.M)
+        # the plain fused kernel's row: | fused AdamW (persistent) [epi 0] | dispatches | busy |
+        m_b = re.search(r"^\| fused (?:AdamW|SGD-m) \(\w+\) \[epi \d+\] \|\s*\d+\s*\|"
+                        r"\s*([0-9.]+)\s*\|", text, re.M)
         if m_sha and m_sha.group(1) == sha and m_b:
             out["mfma_busy_fraction"] = float(m_b.group(1))
     return out or None

@@ -43,9 +43,11 @@ def fake_profiles(tmp_path, monkeypatch):
         "fused_hbm_bytes_per_launch: 3.0e+09\nunfused_pair_hbm_bytes_per_step: 3.7e+09\n"
         "fused_write_bytes: 1.2e+09\n")
     (prof / "pmc_mfma_w.txt").write_text(
-        "kernel_source_sha: abc123\n| kernel | MFMA busy |\n|---|---|\n"
-        "| fused AdamW (persistent) [epi 0] | 0.601 | 1.5e+06 |\n"
-        "| gradient only | 0.679 | 1.3e+06 |\n")
+        "kernel_source_sha: abc123\n| kernel | dispatches | MFMA busy |\n|---|---|---|\n"
+        "| fused AdamW (bf16 m,v, persistent) [epi 8] | 7 | 0.620 | 1.5e+06 |\n"
+        "| fused AdamW (persistent) [epi 0] | 14 | 0.601 | 1.5e+06 |\n"
+        "| fused AdamW from fp8 inputs (X E4M3, dY E5M2, persistent) [epi 32] | 7 | 0.45 |\n"
+        "| gradient (fp32 out, persistent) [epi 2] | 7 | 0.679 | 1.3e+06 |\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
 
 
