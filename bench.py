@@ -44,7 +44,8 @@ WORKLOADS = {
     "moe": (4, "adamw"),
 }
 KERNEL_SOURCES = ("wgrad_kernels.hpp", "elementwise_kernels.hpp", "optim_math.hpp", "forge.hip",
-                  "host.hpp", "host.hip")
+                  "host.hpp", "host.hip", "fp8_kernels.hpp", "forge_fp8.hip", "dgrad_kernels.hpp",
+                  "forge_dgrad.hip")
 
 
 def log(*a):

@@ -154,12 +154,15 @@ __device__ __forceinline__ void wgrad_tile_fp8(const WgradArgs& a, const uint8_t
         acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             frag[f][m], frag[f][TM + n], acc[m][n], FA, FB, 0, 127, 0, 127);
   };
+  // Three transpose reads per MFMA: the next stage's operands are all
+  // requested within the first ~2/3 of the stage's MFMAs, so they have landed
+  // when the barrier waits for them.
   constexpr int NREAD = 4 * (TM + TN);
   auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-      if (2 * i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // DS read
+      if (3 * i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);      // DS read
       if (i < NQW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // VMEM read
     }
   };
