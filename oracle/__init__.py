@@ -38,6 +38,7 @@ from .ref import (  # noqa: F401
     dgrad,
     dgrad_f64,
     grouped_adamw_step,
+    grouped_sgdm_step,
     grouped_wgrad,
     sgdm_step,
     wgrad,

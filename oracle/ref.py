@@ -264,3 +264,15 @@ def grouped_adamw_step(W, m, v, grads, step: int, **hp):
         m_out.append(b_)
         v_out.append(c)
     return np.stack(W_out), np.stack(m_out), np.stack(v_out)
+
+
+def grouped_sgdm_step(W, b, grads, **hp):
+    """SGD-momentum on every expert, including experts that received no
+    tokens (P5 as for AdamW): with g_e = 0 the coupled decay still moves the
+    buffer (b' = momentum b + weight_decay W) and so the weight."""
+    W_out, b_out = [], []
+    for e in range(len(grads)):
+        w_new, b_new = sgdm_step(W[e], b[e], grads[e], **hp)
+        W_out.append(w_new)
+        b_out.append(b_new)
+    return np.stack(W_out), np.stack(b_out)

@@ -312,6 +312,34 @@ def test_grouped_step_decays_empty_experts():
     assert np.array_equal(bits(W1[0]), bits(Wd)) and np.array_equal(bits(v1[0]), bits(vd))
 
 
+def test_grouped_sgdm_moves_empty_experts_by_decay_only():
+    """SGD-momentum on routed experts (P5): an empty expert with no momentum
+    history and no decay stays put exactly; with decay it shrinks toward zero
+    (every element keeps its sign and loses magnitude), and with a momentum
+    history it keeps moving along it; a non-empty expert is the dense step on
+    its own rows."""
+    E, d_out, d_in = 3, 4, 8
+    W = normal_f32(110, (E, d_out, d_in), 0.02)
+    Xb = normal_bf16(113, (6, d_in))
+    dYb = normal_bf16(114, (6, d_out))
+    grads = oracle.grouped_wgrad(Xb, dYb, [0, 6, 6, 6])
+    zero = np.zeros_like(W)
+    W1, b1 = oracle.grouped_sgdm_step(W, zero, grads, lr=1e-3, momentum=0.9, weight_decay=0.0)
+    for e in (1, 2):
+        assert np.array_equal(bits(W1[e]), bits(W[e])) and not np.any(b1[e])
+    W2, b2 = oracle.grouped_sgdm_step(W, zero, grads, lr=1e-2, momentum=0.9, weight_decay=0.5)
+    for e in (1, 2):
+        assert np.all(np.sign(W2[e]) == np.sign(W[e]))
+        assert np.all(np.abs(W2[e]) < np.abs(W[e]))
+    hist = normal_f32(115, W.shape, 1e-3)
+    W3, _ = oracle.grouped_sgdm_step(W, hist, grads, lr=1e-3, momentum=0.9, weight_decay=0.0)
+    for e in (1, 2):
+        assert np.all(np.sign(W[e] - W3[e]) == np.sign(hist[e]))
+    Wd, bd = oracle.sgdm_step(W[0], zero[0], oracle.wgrad(Xb, dYb), lr=1e-2, momentum=0.9,
+                              weight_decay=0.5)
+    assert np.array_equal(bits(W2[0]), bits(Wd)) and np.array_equal(bits(b2[0]), bits(bd))
+
+
 # --------------------------------------------------------------------------
 # accumulation floor and the judge
 # --------------------------------------------------------------------------
