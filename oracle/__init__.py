@@ -46,4 +46,5 @@ from .ref import (  # noqa: F401
     wgrad_rows,
 )
 from .lowp import E4M3, E5M2, acc_floor_fp8, fp8_to_f64, wgrad_fp8, wgrad_fp8_f64  # noqa: F401
-from .floor import StateFloor, acc_floor, acc_floor_rows, dgrad_floor  # noqa: F401
+from .floor import (StateFloor, acc_floor, acc_floor_rows, dgrad_floor,  # noqa: F401
+                    sgdm_arith_floor)

@@ -64,7 +64,9 @@ class StateFloor:
         self.g_hist: list = []
         self.tau_hist: list = []
 
-    def update(self, tau: np.ndarray, g_ref: np.ndarray) -> None:
+    def update(self, tau: np.ndarray, g_ref: np.ndarray, arith=None) -> None:
+        """One step's floors. arith: the rounding floor of the step's own
+        float32 state arithmetic (sgdm_arith_floor), carried on like tau."""
         tau = np.asarray(tau, dtype=np.float64)
         self.g_hist.append(np.asarray(g_ref, dtype=np.float32))
         self.tau_hist.append(tau.astype(np.float32))
@@ -76,3 +78,18 @@ class StateFloor:
             self.m_err = self.momentum * self.m_err + tau
         else:
             raise ValueError(self.kind)
+        if arith is not None:
+            self.m_err = self.m_err + np.asarray(arith, dtype=np.float64)
+
+
+def sgdm_arith_floor(b_prev, g, W_prev, momentum: float, weight_decay: float) -> np.ndarray:
+    """Rounding floor of one float32 momentum update b = momentum b + (g + wd W)
+    itself: whatever the order or fusion of its multiply-adds, each of at most
+    three roundings is within u of a term no larger than momentum |b| + |g| +
+    wd |W|; 4 u times that sum bounds them (the moment floor of the mixed
+    AdamW judgment has the same form). It matters where the terms cancel,
+    e.g. a routed expert with no tokens whose decay and momentum history
+    nearly balance."""
+    return 4.0 * U32 * (momentum * np.abs(np.asarray(b_prev, dtype=np.float64))
+                        + np.abs(np.asarray(g, dtype=np.float64))
+                        + weight_decay * np.abs(np.asarray(W_prev, dtype=np.float64)))

@@ -94,7 +94,8 @@ class SgdmParity:
         self.floor = oracle.StateFloor(self.Wr.shape, "sgdm", momentum=hp["momentum"])
 
     def step(self, g_ref, tau, W_prev_gpu, W_gpu, b_gpu):
-        self.floor.update(tau, g_ref)
+        self.floor.update(tau, g_ref, oracle.sgdm_arith_floor(
+            self.br, g_ref, self.Wr, self.hp["momentum"], self.hp.get("weight_decay", 0.0)))
         Wr_new, br = oracle.sgdm_step(self.Wr, self.br, g_ref, **self.hp)
         rep = judge.judge_sgdm(W_prev_gpu, W_gpu, b_gpu, self.Wr, Wr_new, br, self.floor,
                                self.hp["lr"])

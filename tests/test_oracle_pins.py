@@ -340,6 +340,35 @@ def test_grouped_sgdm_moves_empty_experts_by_decay_only():
     assert np.array_equal(bits(W2[0]), bits(Wd)) and np.array_equal(bits(b2[0]), bits(bd))
 
 
+def test_sgdm_judge_arithmetic_floor():
+    """With an exact gradient (tau = 0) the SGD-momentum judgment accepts a
+    buffer formed with fused multiply-adds where momentum b and wd W cancel,
+    and still rejects a wrong momentum and a dropped decay term."""
+    n = 1 << 16
+    W = normal_f32(120, (n,), 0.02)
+    b = normal_f32(121, (n,), 1e-3)
+    g = np.zeros(n, dtype=F32)
+    hp = dict(lr=1e-3, momentum=0.9, weight_decay=0.01)
+    b[:256] = (-F32(0.01) * W[:256] / F32(0.9)).astype(F32)        # near cancellation
+    W_ref, b_ref = oracle.sgdm_step(W, b, g, **hp)
+    # one rounding of momentum b + wd W, as a fused multiply-add gives
+    b_fma = (0.9 * b.astype(np.float64) + (F32(0.01) * W).astype(np.float64)).astype(F32)
+    W_fma = (W - F32(1e-3) * b_fma).astype(F32)
+
+    def run(b_gpu, W_gpu, arith=True):
+        fl = oracle.StateFloor((n,), "sgdm", momentum=0.9)
+        fl.update(np.zeros(n), g, oracle.sgdm_arith_floor(b, g, W, 0.9, 0.01) if arith else None)
+        return judge.judge_sgdm(W, W_gpu, b_gpu, W, W_ref, b_ref, fl, 1e-3)
+
+    assert not np.array_equal(bits(b_fma), bits(b_ref))           # the two roundings differ
+    assert not run(b_fma, W_fma, arith=False).passed               # so the floor is needed
+    assert run(b_fma, W_fma).passed
+    W_bad, b_bad = oracle.sgdm_step(W, b, g, lr=1e-3, momentum=0.89, weight_decay=0.01)
+    assert not run(b_bad, W_bad).passed
+    W_bad, b_bad = oracle.sgdm_step(W, b, g, lr=1e-3, momentum=0.9, weight_decay=0.0)
+    assert not run(b_bad, W_bad).passed
+
+
 # --------------------------------------------------------------------------
 # accumulation floor and the judge
 # --------------------------------------------------------------------------
