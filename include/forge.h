@@ -220,6 +220,18 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
                                        const forge_adamw_params* p, forge_tile tile, void* stream);
 
 /*
+ * The same with SGD-momentum: mom [E, d_out, d_in] float32 in place of m, v.
+ * An expert with no rows still takes the step with a zero gradient, so the
+ * coupled decay moves its buffer (mom = momentum mom + weight_decay W) and its
+ * weight (same P5 reasoning). Contract otherwise as forge_grouped_wgrad_adamw
+ * and forge_wgrad_sgdm.
+ */
+FORGE_API forge_status forge_grouped_wgrad_sgdm(const void* X_perm, const void* dY_perm,
+                                      const int64_t* offsets, int32_t E, float* W, float* mom,
+                                      int64_t d_in, int64_t d_out, const forge_sgdm_params* p,
+                                      forge_tile tile, void* stream);
+
+/*
  * Precision variants. FORGE assessment, "What's already in tree and easy to
  * miss": the existing lowering accumulates a bf16 matmul in float32 and then
  * truncates to bf16, and that truncation is exactly the rounding the fused

@@ -36,7 +36,7 @@ def declared_symbols(root):
 def test_every_declared_symbol_is_exported(lib, root):
     names = declared_symbols(root)
     assert names == sorted(["forge_adamw", "forge_adamw_mixed", "forge_dgrad",
-                            "forge_dgrad_bf16w", "forge_grouped_wgrad_adamw",
+                            "forge_dgrad_bf16w", "forge_grouped_wgrad_adamw", "forge_grouped_wgrad_sgdm",
                             "forge_linear_backward_adamw", "forge_linear_backward_adamw_bf16w",
                             "forge_linear_backward_sgdm", "forge_linear_backward_sgdm_bf16w",
                             "forge_sgdm", "forge_status_string",
@@ -123,6 +123,8 @@ def test_no_gpu_means_device_error(lib):
     offs = (ctypes.c_int64 * 3)(0, 10, 10)
     assert lib.forge_grouped_wgrad_adamw(X_ADDR, Y_ADDR, offs, 2, A, B, C, 64, 32,
                                          ctypes.byref(adam()), 0, None) == 8
+    assert lib.forge_grouped_wgrad_sgdm(X_ADDR, Y_ADDR, offs, 2, A, B, 64, 32,
+                                        ctypes.byref(sgd()), 0, None) == 8
     assert lib.forge_wgrad_bf16(X_ADDR, Y_ADDR, A, 64, 64, 32, 0, None) == 8
     assert lib.forge_wgrad_adamw_bf16state(X_ADDR, Y_ADDR, A, B, C, 64, 64, 32,
                                            ctypes.byref(adam()), 0, None) == 8
@@ -334,6 +336,25 @@ def test_grouped_rejects(lib):
     assert call([0, 4, 9], d_in=36) == 3
     assert call([0, 4, 9], m=A + 64 * 32 * 4) == 4   # m overlaps expert 1 of W
     assert call([0, 4, 9], p=adam(max_grad_norm=1.0)) == 6
+
+
+def test_grouped_sgdm_rejects(lib):
+    def call(offs, W=A, mom=B, d_in=64, d_out=32, p=None, tile=0):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        p = sgd() if p is None else p
+        return lib.forge_grouped_wgrad_sgdm(X_ADDR, Y_ADDR, arr, len(offs) - 1, W, mom, d_in,
+                                            d_out, ctypes.byref(p), tile, None)
+
+    assert lib.forge_grouped_wgrad_sgdm(X_ADDR, Y_ADDR, None, 2, A, B, 64, 32,
+                                        ctypes.byref(sgd()), 0, None) == 1
+    assert call([0, 4, 9], mom=NULL) == 1
+    assert call([0, 9, 4]) == 2
+    assert call([0, 4, 9], d_out=36) == 3
+    assert call([0, 4, 9], mom=A + 64 * 32 * 4) == 4     # mom overlaps expert 1 of W
+    assert call([0, 4, 9], p=sgd(max_grad_norm=0.5)) == 6
+    assert call([0, 4, 9], p=sgd(momentum=1.0)) == 5
+    assert call([0, 4, 9], tile=9) == 7
+    assert call([0, 4, 9], d_in=0) == 0                   # nothing to update
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

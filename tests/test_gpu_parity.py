@@ -10,8 +10,8 @@ import pytest
 import oracle
 import synth
 from synth import DenseCase
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, log,
-                        run_dense_adamw, run_dense_sgdm, torch_mod)
+from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
+                        log, run_dense_adamw, run_dense_sgdm, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,6 +215,46 @@ def test_grouped_small_with_empty_experts(wg):
             rep = pars[e].step(t, grads[e], tau, W_prev[e], Wg[e], mg[e], vg[e])
             assert rep.passed, f"expert {e} step {t}: {rep}"
         assert not bits_equal(Wg[1], W_prev[1])   # the empty expert still moved
+
+
+def test_grouped_sgdm_with_empty_experts(wg):
+    """SGD-momentum on routed experts: each expert judged against the oracle's
+    step on its own rows; the empty expert moves by its decay and momentum;
+    each expert bitwise the dense call on its rows."""
+    torch = torch_mod()
+    E, d_in, d_out = 4, 136, 264
+    offsets = [0, 37, 37, 100, 117]           # expert 1 empty, ragged counts
+    hp = dict(lr=1e-3, momentum=0.9, weight_decay=0.01)
+    W0 = synth.normal_f32(90, (E, d_out, d_in), 0.02)
+    b0 = synth.normal_f32(91, W0.shape, 1e-3)    # a momentum history
+    for tile in (1, 2, 3):
+        W, b = f32_dev(W0), f32_dev(b0)
+        pars = [SgdmParity(W0[e], b0[e], hp) for e in range(E)]
+        for t in (1, 2):
+            log(f"[grouped sgdm] tile {tile} step {t}")
+            Xb = synth.normal_bf16(93 + t, (offsets[-1], d_in))
+            dYb = synth.normal_bf16(97 + t, (offsets[-1], d_out))
+            W_prev, b_prev = host(W), host(b)
+            wg.forge_grouped_wgrad_sgdm(bf16_dev(Xb), bf16_dev(dYb), offsets, W, b, tile=tile,
+                                        **hp)
+            _sync()
+            Wg, bg = host(W), host(b)
+            grads = oracle.grouped_wgrad(Xb, dYb, offsets)
+            for e in range(E):
+                a, c = offsets[e], offsets[e + 1]
+                tau = oracle.acc_floor(Xb[a:c], dYb[a:c]) if c > a else np.zeros((d_out, d_in))
+                rep = pars[e].step(grads[e], tau, W_prev[e], Wg[e], bg[e])
+                assert rep.passed, f"expert {e} step {t}: {rep}"
+                Wd, bd = f32_dev(W_prev[e]), f32_dev(b_prev[e])
+                Xe = bf16_dev(Xb[a:c]) if c > a else torch.empty((0, d_in), dtype=torch.bfloat16,
+                                                                  device="cuda")
+                dYe = bf16_dev(dYb[a:c]) if c > a else torch.empty((0, d_out),
+                                                                    dtype=torch.bfloat16,
+                                                                    device="cuda")
+                wg.forge_wgrad_sgdm(Xe, dYe, Wd, bd, tile=1, **hp)
+                _sync()
+                assert bits_equal(Wg[e], host(Wd)) and bits_equal(bg[e], host(bd)), (tile, e)
+            assert not bits_equal(Wg[1], W_prev[1])     # the empty expert still moved
 
 
 def test_grouped_expert_equals_dense_call(wg):

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     forge_dgrad,
     forge_dgrad_bf16w,
     forge_grouped_wgrad_adamw,
+    forge_grouped_wgrad_sgdm,
     forge_linear_backward_adamw,
     forge_linear_backward_adamw_bf16w,
     forge_linear_backward_sgdm,

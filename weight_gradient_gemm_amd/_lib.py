@@ -92,6 +92,9 @@ def library() -> ctypes.CDLL:
         lib.forge_linear_backward_sgdm_bf16w.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, ctypes.POINTER(SgdmParams),
             _i32, _vp]
+        lib.forge_grouped_wgrad_sgdm.argtypes = [_vp, _vp, ctypes.POINTER(_i64), _i32, _vp, _vp,
+                                                 _i64, _i64, ctypes.POINTER(SgdmParams), _i32,
+                                                 _vp]
         lib.forge_wgrad_adamw_bf16w.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                                 ctypes.POINTER(AdamWParams), _i32, _vp]
         lib.forge_wgrad_sgdm_bf16w.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
@@ -109,7 +112,8 @@ def library() -> ctypes.CDLL:
                      "forge_linear_backward_adamw", "forge_linear_backward_sgdm",
                      "forge_wgrad_fp8", "forge_wgrad_adamw_fp8", "forge_dgrad_bf16w",
                      "forge_linear_backward_adamw_bf16w", "forge_linear_backward_sgdm_bf16w",
-                     "forge_wgrad_adamw_bf16w", "forge_wgrad_sgdm_bf16w"):
+                     "forge_wgrad_adamw_bf16w", "forge_wgrad_sgdm_bf16w",
+                     "forge_grouped_wgrad_sgdm"):
             getattr(lib, name).restype = _i32
         _LIB = lib
     return _LIB
@@ -277,13 +281,8 @@ def forge_sgdm(grad, W, mom, *, lr=1e-3, momentum=0.9, weight_decay=0.0, max_gra
                                 _stream(stream)), "forge_sgdm")
 
 
-def forge_grouped_wgrad_adamw(X_perm, dY_perm, offsets, W, m, v, *, step, lr=1e-3, beta1=0.9,
-                              beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
-                              tile=FORGE_TILE_DEFAULT, stream=None) -> None:
-    """AdamW on E routed experts; expert e contracts rows offsets[e]:offsets[e+1].
-
-    ``offsets`` is a host sequence of E+1 ints. Experts with no rows still
-    take the step (zero gradient)."""
+def _grouped_args(X_perm, dY_perm, offsets, W, others):
+    """Routed rows and host offsets; W and the state [E, d_out, d_in] float32."""
     torch = _torch()
     _want(X_perm, torch.bfloat16, "X_perm")
     _want(dY_perm, torch.bfloat16, "dY_perm")
@@ -297,13 +296,36 @@ def forge_grouped_wgrad_adamw(X_perm, dY_perm, offsets, W, m, v, *, step, lr=1e-
         raise ValueError("offsets must hold E+1 >= 2 entries")
     if offs[-1] != R:
         raise ValueError(f"offsets[E] = {offs[-1]} but X_perm has {R} rows")
-    _state_like(W, (("m", m), ("v", v)), d_out, d_in, lead=(E,))
-    arr = (_i64 * (E + 1))(*offs)
+    _state_like(W, others, d_out, d_in, lead=(E,))
+    return (_i64 * (E + 1))(*offs), E, d_in, d_out
+
+
+def forge_grouped_wgrad_adamw(X_perm, dY_perm, offsets, W, m, v, *, step, lr=1e-3, beta1=0.9,
+                              beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                              tile=FORGE_TILE_DEFAULT, stream=None) -> None:
+    """AdamW on E routed experts; expert e contracts rows offsets[e]:offsets[e+1].
+
+    ``offsets`` is a host sequence of E+1 ints. Experts with no rows still
+    take the step (zero gradient)."""
+    arr, E, d_in, d_out = _grouped_args(X_perm, dY_perm, offsets, W, (("m", m), ("v", v)))
     p = _adamw(step, lr, beta1, beta2, eps, weight_decay, max_grad_norm)
     _check(library().forge_grouped_wgrad_adamw(_ptr(X_perm), _ptr(dY_perm), arr, E, _ptr(W),
                                                _ptr(m), _ptr(v), d_in, d_out, ctypes.byref(p),
                                                int(tile), _stream(stream)),
            "forge_grouped_wgrad_adamw")
+
+
+def forge_grouped_wgrad_sgdm(X_perm, dY_perm, offsets, W, mom, *, lr=1e-3, momentum=0.9,
+                             weight_decay=0.0, max_grad_norm=0.0, tile=FORGE_TILE_DEFAULT,
+                             stream=None) -> None:
+    """SGD-momentum on E routed experts; experts with no rows still take the
+    step (zero gradient, so only the coupled decay and the momentum move them)."""
+    arr, E, d_in, d_out = _grouped_args(X_perm, dY_perm, offsets, W, (("mom", mom),))
+    p = SgdmParams(float(lr), float(momentum), float(weight_decay), float(max_grad_norm))
+    _check(library().forge_grouped_wgrad_sgdm(_ptr(X_perm), _ptr(dY_perm), arr, E, _ptr(W),
+                                              _ptr(mom), d_in, d_out, ctypes.byref(p), int(tile),
+                                              _stream(stream)),
+           "forge_grouped_wgrad_sgdm")
 
 
 # --------------------------------------------------------------------------

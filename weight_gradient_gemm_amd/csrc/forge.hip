@@ -165,6 +165,31 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
   return with_adamw_epi<GroupedLaunch>(*p, a, gt, E, tile, static_cast<hipStream_t>(stream));
 }
 
+FORGE_API forge_status forge_grouped_wgrad_sgdm(const void* X_perm, const void* dY_perm,
+                                                const int64_t* offsets, int32_t E, float* W,
+                                                float* mom, int64_t d_in, int64_t d_out,
+                                                const forge_sgdm_params* p, forge_tile tile,
+                                                void* stream) {
+  if (forge_status s = validate_grouped_sgdm(X_perm, dY_perm, offsets, E, W, mom, d_in, d_out, p,
+                                             tile))
+    return s;
+  if (d_in == 0 || d_out == 0) return FORGE_OK;
+  if (forge_status s = check_device()) return s;
+  tile = resolve_tile(tile, d_in, d_out, E);
+  if (!grid_fits(d_in, d_out, tile, E)) return FORGE_ERR_SHAPE;
+  (void)hipGetLastError();
+  GroupTable gt;
+  std::memset(&gt, 0, sizeof(gt));
+  for (int32_t e = 0; e <= E; ++e) gt.off[e] = offsets[e];
+  for (int32_t e = 0; e < E; ++e) gt.order[e] = e;
+  std::stable_sort(gt.order, gt.order + E, [&](int32_t x, int32_t y) {
+    return offsets[x + 1] - offsets[x] > offsets[y + 1] - offsets[y];
+  });
+  WgradArgs a = base_args(X_perm, dY_perm, W, mom, nullptr, 0, d_in, d_out);
+  a.sgd = make_sgdm(*p);
+  return GroupedLaunch<EPI_SGDM>::run(a, gt, E, tile, static_cast<hipStream_t>(stream));
+}
+
 FORGE_API forge_status forge_wgrad_bf16(const void* X, const void* dY, void* grad_bf16,
                                         int64_t T, int64_t d_in, int64_t d_out, forge_tile tile,
                                         void* stream) {

@@ -250,6 +250,17 @@ forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
   return check_tile(tile);
 }
 
+forge_status validate_grouped_sgdm(const void* X_perm, const void* dY_perm,
+                                   const int64_t* offsets, int32_t E, const float* W,
+                                   const float* mom, int64_t d_in, int64_t d_out,
+                                   const forge_sgdm_params* p, forge_tile tile) {
+  const void* outs[2] = {W, mom};
+  if (!p) return FORGE_ERR_NULL;
+  if (forge_status s = check_grouped(X_perm, dY_perm, offsets, E, outs, 2, d_in, d_out)) return s;
+  if (forge_status s = check_sgdm_params(p)) return s;
+  return check_tile(tile);
+}
+
 namespace {
 
 bool is_fp8(forge_dtype t) { return t == FORGE_FP8_E4M3 || t == FORGE_FP8_E5M2; }

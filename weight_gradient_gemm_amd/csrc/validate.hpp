@@ -106,6 +106,10 @@ forge_status validate_grouped_adamw(const void* X_perm, const void* dY_perm,
                                     const int64_t* offsets, int32_t E, const float* W,
                                     const float* m, const float* v, int64_t d_in, int64_t d_out,
                                     const forge_adamw_params* p, forge_tile tile);
+forge_status validate_grouped_sgdm(const void* X_perm, const void* dY_perm,
+                                   const int64_t* offsets, int32_t E, const float* W,
+                                   const float* mom, int64_t d_in, int64_t d_out,
+                                   const forge_sgdm_params* p, forge_tile tile);
 
 // Largest d_in and d_out: one LDS stage of token rows must stay within a
 // 31-bit byte window (32-bit row/column indices, 64-bit element offsets).

@@ -710,8 +710,9 @@ void wgrad_grouped_kernel(WgradArgs a, GroupTable gt) {
            tm, tn);
   const int64_t r0 = gt.off[e], r1 = gt.off[e + 1];
   const int64_t state = int64_t(e) * a.d_out * a.d_in;
-  wgrad_tile<C, EPI>(a, a.X + r0 * a.d_in, a.dY + r0 * a.d_out, a.W + state, a.S1 + state,
-                     a.S2 + state, r1 - r0, tm, tn, ring);
+  float* const s2 = is_adamw(EPI) ? a.S2 + state : nullptr;   // SGD-m has no second buffer
+  wgrad_tile<C, EPI>(a, a.X + r0 * a.d_in, a.dY + r0 * a.d_out, a.W + state, a.S1 + state, s2,
+                     r1 - r0, tm, tn, ring);
 }
 
 // Persistent schedule. One workgroup per CU walks a list of items, each a full
