@@ -120,6 +120,7 @@ def library() -> ctypes.CDLL:
 
 
 def forge_status_string(status: int) -> str:
+    """The library's text for a status code (unknown codes get a generic text)."""
     return library().forge_status_string(int(status)).decode()
 
 
