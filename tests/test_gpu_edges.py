@@ -90,3 +90,21 @@ def test_smallest_shapes(wg, T, d_in, d_out, tile):
     _sync()
     err = np.abs(host(g).astype(np.float64) - oracle.wgrad_f64(Xb, dYb))
     assert np.all(err <= oracle.acc_floor(Xb, dYb))
+
+
+def test_tensor_on_another_device_is_refused(wg, monkeypatch):
+    """The binding refuses tensors that are not on the current device (the
+    launch would touch another GPU's memory) before calling the library."""
+    torch = torch_mod()
+    X = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    dY = torch.zeros((16, 32), dtype=torch.bfloat16, device="cuda")
+    W, m, v = (torch.zeros((32, 64), device="cuda") for _ in range(3))
+    real = torch.cuda.current_device()
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: real + 1)
+    with pytest.raises(ValueError, match="current device"):
+        wg.forge_wgrad_adamw(X, dY, W, m, v, step=1)
+    monkeypatch.undo()
+    wg.forge_wgrad_adamw(X, dY, W, m, v, step=1)
+    _sync()
+    assert not np.any(host(m)) and bits_equal(host(W), np.zeros((32, 64), np.float32))
+

@@ -155,6 +155,11 @@ def _want(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        # the library launches on the current device; another device's memory would fault
+        raise ValueError(f"{name} is on {t.device} but the current device is cuda:{cur} "
+                         "(select it with torch.cuda.device)")
 
 
 def _stream(stream):
