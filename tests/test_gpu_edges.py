@@ -93,8 +93,9 @@ def test_smallest_shapes(wg, T, d_in, d_out, tile):
 
 
 def test_tensor_on_another_device_is_refused(wg, monkeypatch):
-    """The binding refuses tensors that are not on the current device (the
-    launch would touch another GPU's memory) before calling the library."""
+    """The binding refuses tensors and streams that are not on the current
+    device (the launch would touch another GPU's memory) before calling the
+    library; on the right device the same call runs."""
     torch = torch_mod()
     X = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     dY = torch.zeros((16, 32), dtype=torch.bfloat16, device="cuda")
@@ -103,8 +104,13 @@ def test_tensor_on_another_device_is_refused(wg, monkeypatch):
     monkeypatch.setattr(torch.cuda, "current_device", lambda: real + 1)
     with pytest.raises(ValueError, match="current device"):
         wg.forge_wgrad_adamw(X, dY, W, m, v, step=1)
+    s = torch.cuda.Stream()                         # a stream of the real device
+    with pytest.raises(ValueError, match="current device"):
+        wg._lib._stream(s)
     monkeypatch.undo()
-    wg.forge_wgrad_adamw(X, dY, W, m, v, step=1)
+    wg.forge_wgrad_adamw(X, dY, W, m, v, step=1, stream=s)
+    s.synchronize()
+    wg.forge_wgrad_adamw(X, dY, W, m, v, step=2)
     _sync()
     assert not np.any(host(m)) and bits_equal(host(W), np.zeros((32, 64), np.float32))
 

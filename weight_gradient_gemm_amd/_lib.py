@@ -166,6 +166,9 @@ def _stream(stream):
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {stream.device} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
