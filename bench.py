@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA, twice the bf16 rate
+NOMINAL_CLOCK_GHZ = 2.4        # the clock the published peaks are quoted at
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused dW-GEMM+AdamW TFLOP/s & ms/step, MFMA util %, HBM bytes vs unfused"
 
@@ -105,10 +106,18 @@ def read_counters(workload: str, sha: str, n_param: int):
             text = f.read()
         m_sha = re.search(r"^kernel_source_sha:\s*(\w+)", text, re.M)
         # the plain fused kernel's row: | fused AdamW (persistent) [epi 0] | dispatches | busy |
+        # cycles per XCD | mean us | clock GHz | ...
         m_b = re.search(r"^\| fused (?:AdamW|SGD-m) \(\w+\) \[epi \d+\] \|\s*\d+\s*\|"
-                        r"\s*([0-9.]+)\s*\|", text, re.M)
+                        r"\s*([0-9.]+)\s*\|(?:\s*[0-9.eE+]+\s*\|\s*[0-9.]+\s*\|\s*([0-9.]+)\s*\|)?",
+                        text, re.M)
         if m_sha and m_sha.group(1) == sha and m_b:
             out["mfma_busy_fraction"] = float(m_b.group(1))
+            if m_b.group(2):
+                # The board holds this kernel at its power limit below the nominal
+                # clock; the busy fraction is against the peak at the clock it ran.
+                clock = float(m_b.group(2))
+                out["clock_ghz"] = clock
+                out["peak_tflops_at_clock"] = round(PEAK_BF16_TFLOPS * clock / NOMINAL_CLOCK_GHZ, 1)
     return out or None
 
 

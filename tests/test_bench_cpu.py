@@ -45,7 +45,7 @@ def fake_profiles(tmp_path, monkeypatch):
     (prof / "pmc_mfma_w.txt").write_text(
         "kernel_source_sha: abc123\n| kernel | dispatches | MFMA busy |\n|---|---|---|\n"
         "| fused AdamW (bf16 m,v, persistent) [epi 8] | 7 | 0.620 | 1.5e+06 |\n"
-        "| fused AdamW (persistent) [epi 0] | 14 | 0.601 | 1.5e+06 |\n"
+        "| fused AdamW (persistent) [epi 0] | 14 | 0.601 | 1.5e+06 | 900.0 | 1.80 | 3e+07 |\n"
         "| fused AdamW from fp8 inputs (X E4M3, dY E5M2, persistent) [epi 32] | 7 | 0.45 |\n"
         "| gradient (fp32 out, persistent) [epi 2] | 7 | 0.679 | 1.3e+06 |\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
@@ -55,7 +55,8 @@ def test_counters_read_when_the_sources_match(fake_profiles):
     assert bench.read_traffic("w", "abc123") == 3.0e9
     c = bench.read_counters("w", "abc123", 100_000_000)
     assert c == {"fused_write_bytes_per_param": 12.0, "unfused_pair_hbm_bytes": 3.7e9,
-                 "mfma_busy_fraction": 0.601}
+                 "mfma_busy_fraction": 0.601, "clock_ghz": 1.8,
+                 "peak_tflops_at_clock": round(bench.PEAK_BF16_TFLOPS * 1.8 / 2.4, 1)}
 
 
 def test_counters_dropped_when_the_sources_changed(fake_profiles):
