@@ -10,7 +10,8 @@ import pytest
 import oracle
 import synth
 from oracle import judge
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, host_f32,
+from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
+                        host_f32,
                         log, run_dense_adamw, run_dense_sgdm, sample_rows, torch_mod)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -128,6 +129,35 @@ def test_mlp_down_fp8_adamw(wg):
         assert rep.passed, f"step {t}: {rep}"
 
 
+def test_lm_head_fp8_adamw(wg):
+    """fp8 inputs on the LM-head workload (softmax-gradient dY in E5M2, whose
+    small probabilities fall to subnormal codes or zero; 501 tile columns):
+    one fused AdamW step on sampled rows of W (the MLP-down fp8 test covers
+    the state over several steps; encoding these inputs takes most of the
+    time)."""
+    from oracle import lowp
+    torch = torch_mod()
+    case = synth.dense_case(3)
+    rows = sample_rows(case.d_out, per_tile=2, extra=64)
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    par = AdamWParity(W0, m0, v0, hp, rows=rows)
+    for t in range(1, 2):
+        X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, t)
+        log(f"[{case.name}] fp8 adamw step {t}")
+        W_prev = host(W, rows)
+        wg.forge_wgrad_adamw_fp8(torch.from_numpy(X8).to("cuda"), "e4m3", sx,
+                                 torch.from_numpy(dY8).to("cuda"), "e5m2", sdy, W, m, v, step=t,
+                                 **hp)
+        torch.cuda.synchronize()
+        g_ref = lowp.wgrad_fp8(X8, "e4m3", sx, np.ascontiguousarray(dY8[:, rows]), "e5m2", sdy)
+        tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows, exact_max=False)
+        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
+        log(f"  {rep}")
+        assert rep.passed, f"step {t}: {rep}"
+
+
 def test_qkv_adamw_and_sgdm(wg):
     """GQA QKV projection: T=16384, d_in=4096, d_out=6144; AdamW and SGD-momentum."""
     case = synth.dense_case(2)
@@ -195,6 +225,35 @@ def test_moe_grouped_adamw(wg):
     """8 experts W[14336, 4096], T=16384 top-2, Zipf(1.1) loads, two empty experts."""
     case = synth.grouped_case(4)
     _grouped_run(wg, case, case.steps, sample_rows(case.d_out, per_tile=2, extra=16))
+
+
+def test_moe_grouped_sgdm(wg):
+    """SGD-momentum on the routed-expert workload (8 experts W[14336, 4096], two
+    of them empty), 2 steps with decay on sampled rows: each expert against the
+    oracle's step on its own rows; the empty experts move by their decay."""
+    case = synth.grouped_case(4)
+    rows = sample_rows(case.d_out, per_tile=2, extra=16)
+    W0, _, _ = synth.grouped_state(case)
+    b0 = np.zeros_like(W0)
+    hp = dict(lr=case.lr, momentum=0.9, weight_decay=0.01)
+    W, b = f32_dev(W0), f32_dev(b0)
+    pars = [SgdmParity(W0[e], b0[e], hp, rows=rows) for e in range(case.E)]
+    for t in (1, 2):
+        Xp, Yp, offs = synth.grouped_inputs(case, t)
+        log(f"[{case.name}] sgdm step {t} loads {np.diff(offs).tolist()}")
+        W_prev = host(W, rows)
+        wg.forge_grouped_wgrad_sgdm(bf16_dev(Xp), bf16_dev(Yp), offs.tolist(), W, b, **hp)
+        torch_mod().cuda.synchronize()
+        Wg, bg = host(W, rows), host(b, rows)
+        grads = oracle.grouped_wgrad(Xp, Yp, offs, rows=rows)
+        for e in range(case.E):
+            a, c = int(offs[e]), int(offs[e + 1])
+            tau = (oracle.acc_floor_rows(Xp[a:c], Yp[a:c], rows) if c > a
+                   else np.zeros((len(rows), case.d_in)))
+            rep = pars[e].step(grads[e], tau, W_prev[e], Wg[e], bg[e])
+            assert rep.passed, f"expert {e} (rows {c - a}) step {t}: {rep}"
+            if c == a:
+                assert not np.array_equal(Wg[e], W_prev[e])
 
 
 def test_moe_grouped_warm_start(wg):
