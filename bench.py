@@ -19,6 +19,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -121,6 +122,13 @@ def read_counters(workload: str, sha: str, n_param: int):
     return out or None
 
 
+def with_tokens(case, tokens: int):
+    """The dense workload `case` with `tokens` rows of X and dY (same layer,
+    same seeds and distributions); its name carries the new count."""
+    name = re.sub(r"_T\d+$", "", case.name) + f"_T{tokens}"
+    return dataclasses.replace(case, T=int(tokens), name=name)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +143,9 @@ def main():
                     help="skip the precision-variant legs (dense AdamW workloads)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the input-gradient and whole-backward legs (dense AdamW)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="dense workloads: run the layer with this many tokens instead of "
+                         "the workload's own (a token-count sweep; not the headline line)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -156,6 +167,12 @@ def main():
     k, opt = WORKLOADS[args.workload]
     case = synth.CONFIGS[k]
     grouped = isinstance(case, synth.GroupedCase)
+    if args.tokens:
+        if grouped or args.tokens < 1:
+            print("--tokens takes a positive count and applies to dense workloads only",
+                  file=sys.stderr)
+            sys.exit(2)
+        case = with_tokens(case, args.tokens)
 
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(

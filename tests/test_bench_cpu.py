@@ -63,3 +63,11 @@ def test_counters_dropped_when_the_sources_changed(fake_profiles):
     assert bench.read_traffic("w", "other") is None
     assert bench.read_counters("w", "other", 100_000_000) is None
     assert bench.read_traffic("missing", "abc123") is None
+
+
+def test_token_override_keeps_the_layer():
+    import synth
+    base = synth.CONFIGS[1]
+    c = bench.with_tokens(base, 2048)
+    assert (c.T, c.d_in, c.d_out, c.seed_base) == (2048, base.d_in, base.d_out, base.seed_base)
+    assert c.name.endswith("_T2048") and "_T8192" not in c.name
