@@ -64,13 +64,22 @@ def sample_rows(d_out: int, bn: int = 128, per_tile: int = 2, extra: int = 16, s
     return np.array(sorted(rows), dtype=np.int64)
 
 
+# Share of elements that may take the widened weight-delta bar at any step
+# (bf16 inputs): the oracle alone decides the set; measured 0-0.16% on the
+# workloads here (0.16% on QKV at step 2).
+AMBIGUOUS_BUDGET = 0.0025
+
+
 class AdamWParity:
     """Runs AdamW steps on the GPU state and on an oracle copy of (sampled rows
-    of) the state, judging every step."""
+    of) the state, judging every step. ambiguous_budget: see judge_adamw
+    (None: no budget, e.g. for fp8 inputs, whose floor includes the fp8 dot
+    product's deviation)."""
 
-    def __init__(self, W0, m0, v0, hp, rows=None, lead=None):
+    def __init__(self, W0, m0, v0, hp, rows=None, lead=None, ambiguous_budget=AMBIGUOUS_BUDGET):
         self.hp = dict(hp)
         self.rows = rows
+        self.budget = ambiguous_budget
         self.zero_start = not (np.any(m0) or np.any(v0))
         sel = (lambda a: a) if rows is None else (lambda a: a[..., rows, :])
         self.Wr, self.mr, self.vr = sel(W0).copy(), sel(m0).copy(), sel(v0).copy()
@@ -80,7 +89,8 @@ class AdamWParity:
         self.floor.update(tau, g_ref)
         Wr_new, mr, vr = oracle.adamw_step(self.Wr, self.mr, self.vr, g_ref, t, **self.hp)
         rep = judge.judge_adamw(t, W_prev_gpu, W_gpu, m_gpu, v_gpu, self.Wr, Wr_new, mr, vr,
-                                g_ref, tau, self.floor, zero_start=self.zero_start, **self.hp)
+                                g_ref, tau, self.floor, zero_start=self.zero_start,
+                                ambiguous_budget=self.budget, **self.hp)
         self.Wr, self.mr, self.vr = Wr_new, mr, vr
         return rep
 
