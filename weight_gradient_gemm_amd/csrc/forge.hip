@@ -148,7 +148,7 @@ FORGE_API forge_status forge_grouped_wgrad_adamw(const void* X_perm, const void*
     return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
   if (forge_status s = check_device()) return s;
-  tile = resolve_tile(tile, d_in, d_out, E);
+  tile = resolve_tile(tile, d_in, d_out, E, /*allow_persistent=*/false);
   if (!grid_fits(d_in, d_out, tile, E)) return FORGE_ERR_SHAPE;
   (void)hipGetLastError();
   GroupTable gt;
@@ -175,7 +175,7 @@ FORGE_API forge_status forge_grouped_wgrad_sgdm(const void* X_perm, const void* 
     return s;
   if (d_in == 0 || d_out == 0) return FORGE_OK;
   if (forge_status s = check_device()) return s;
-  tile = resolve_tile(tile, d_in, d_out, E);
+  tile = resolve_tile(tile, d_in, d_out, E, /*allow_persistent=*/false);
   if (!grid_fits(d_in, d_out, tile, E)) return FORGE_ERR_SHAPE;
   (void)hipGetLastError();
   GroupTable gt;
