@@ -147,12 +147,6 @@ typedef struct {
  *     tile out of step, which balances a fractional number of tiles per unit
  *     and spreads the optimizer epilogues' HBM traffic over time. Dense calls
  *     only; a grouped call treats it as FORGE_TILE_256x256.
- *   FORGE_TILE_PINGPONG: one workgroup of two 4-wave groups per compute unit;
- *     each group walks its own list of 256x128 tiles and the second trails the
- *     first by one epilogue, so one group's optimizer epilogue runs while the
- *     other group's contraction keeps the matrix cores busy. Dense calls only
- *     (a grouped call or the input gradient treats it as FORGE_TILE_256x256;
- *     the fp8-input and bf16-state calls as FORGE_TILE_PERSISTENT).
  */
 typedef int32_t forge_tile;
 enum {
@@ -161,8 +155,7 @@ enum {
   FORGE_TILE_128x128 = 2,
   FORGE_TILE_256x256 = 3,
   FORGE_TILE_PERSISTENT = 4,
-  FORGE_TILE_PINGPONG = 5,
-  FORGE_TILE_COUNT = 6
+  FORGE_TILE_COUNT = 5
 };
 
 /* Maximum number of experts in one grouped call. */

@@ -34,7 +34,7 @@ def _sync():
     torch_mod().cuda.synchronize()
 
 
-@pytest.mark.parametrize("tile", [0, 4, 5])
+@pytest.mark.parametrize("tile", [0, 4])
 def test_split_run_equals_whole_run(wg, tile):
     case = DenseCase("split_300x520x392", T=300, d_in=520, d_out=392, seed_base=66000, steps=10)
     hp = adamw_hp(case)
@@ -59,7 +59,7 @@ def test_split_run_equals_whole_run(wg, tile):
 
 
 @pytest.mark.parametrize("T,d_in,d_out", [(1, 8, 8), (4, 8, 8), (8, 16, 8), (17, 8, 24)])
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 def test_smallest_shapes(wg, T, d_in, d_out, tile):
     torch = torch_mod()
     case = DenseCase(f"tiny_{T}x{d_in}x{d_out}", T=T, d_in=d_in, d_out=d_out,

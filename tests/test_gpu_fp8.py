@@ -166,7 +166,7 @@ def test_wgrad_fp8_matches_the_model_within_the_fp32_floor(wg, fx, fy):
 
 
 @pytest.mark.parametrize("fx,fy", FMTS)
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", [RAGGED, MANY], ids=lambda c: c.name)
 def test_wgrad_fp8_against_oracle(wg, case, tile, fx, fy):
     X8, sx, dY8, sdy = _inputs(case, 1, fx, fy)

@@ -193,7 +193,7 @@ def test_qkv_bitwise_across_tilings_full_tensors(wg):
     X, dY = bf16_dev(Xb), bf16_dev(dYb)
     W0, m0, v0 = synth.dense_state(case)
     out = []
-    tiles = (1, 2, 3, 4, 5, 1)
+    tiles = (1, 2, 3, 4, 1)
     for tile in tiles:
         W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
         log(f"[qkv bitwise] tile {tile}")

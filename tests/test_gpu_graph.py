@@ -61,7 +61,7 @@ def _replay_and_check(g, live, initial, expected, between):
             assert bits_equal(host_f32(t), e), f"replay {r}"
 
 
-@pytest.mark.parametrize("tile", [0, 3, 4, 5])
+@pytest.mark.parametrize("tile", [0, 3, 4])
 def test_fused_adamw_steps_replay(wg, tile):
     torch = torch_mod()
     hp = adamw_hp(CASE)

@@ -51,7 +51,7 @@ RAGGED = DenseCase("ragged_77x264x200", T=77, d_in=264, d_out=200, seed_base=570
 MANY = DenseCase("tiles_300x520x392", T=300, d_in=520, d_out=392, seed_base=58000, steps=2)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", [RAGGED, MANY], ids=lambda c: c.name)
 def test_wgrad_bf16_against_oracle(wg, case, tile):
     torch = torch_mod()
@@ -142,7 +142,7 @@ def _run_variant_dense(wg, case, tile, grad_bf16, state_bf16, steps, fused=True)
     return W, m, v
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 def test_fused_bf16_state(wg, tile):
     _run_variant_dense(wg, RAGGED, tile, False, True, RAGGED.steps)
 

@@ -11,7 +11,6 @@ from ._lib import (  # noqa: F401
     FORGE_TILE_256x128,
     FORGE_TILE_256x256,
     FORGE_TILE_PERSISTENT,
-    FORGE_TILE_PINGPONG,
     FORGE_TILE_DEFAULT,
     FORGE_BF16,
     FORGE_F32,

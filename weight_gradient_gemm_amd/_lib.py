@@ -18,7 +18,6 @@ FORGE_TILE_256x128 = 1
 FORGE_TILE_128x128 = 2
 FORGE_TILE_256x256 = 3
 FORGE_TILE_PERSISTENT = 4
-FORGE_TILE_PINGPONG = 5
 
 FORGE_F32 = 0
 FORGE_BF16 = 1

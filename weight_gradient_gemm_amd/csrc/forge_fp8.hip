@@ -21,8 +21,7 @@ forge_status launch_fp8_t(WgradArgs a, forge_tile tile, hipStream_t s) {
     case FORGE_TILE_128x128: return launch_fp8_dense_t<Cfg128x128, EPI, FA, FB>(a, s);
     case FORGE_TILE_256x128: return launch_fp8_dense_t<Cfg256x128, EPI, FA, FB>(a, s);
     case FORGE_TILE_256x256: return launch_fp8_dense_t<Cfg256x256, EPI, FA, FB>(a, s);
-    case FORGE_TILE_PERSISTENT:
-    case FORGE_TILE_PINGPONG: {
+    case FORGE_TILE_PERSISTENT: {
       set_grid<Cfg256x256>(a, 1);
       const int grid = persistent_grid();
       if (grid <= 0) return launch_fp8_dense_t<Cfg256x256, EPI, FA, FB>(a, s);

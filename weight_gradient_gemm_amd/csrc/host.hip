@@ -78,7 +78,6 @@ TileShape shape_of(forge_tile t) {
     case FORGE_TILE_256x256:
     case FORGE_TILE_PERSISTENT: return {256, 256};
     case FORGE_TILE_256x128:
-    case FORGE_TILE_PINGPONG:
     default: return {256, 128};
   }
 }
@@ -113,9 +112,7 @@ double persistent_makespan(int64_t tiles, int grid) {
 
 forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts,
                         bool allow_persistent) {
-  if ((experts > 1 || !allow_persistent) &&
-      (t == FORGE_TILE_PERSISTENT || t == FORGE_TILE_PINGPONG))
-    return FORGE_TILE_256x256;
+  if ((experts > 1 || !allow_persistent) && t == FORGE_TILE_PERSISTENT) return FORGE_TILE_256x256;
   if (t != FORGE_TILE_DEFAULT) return t;
   struct Cand {
     forge_tile id;

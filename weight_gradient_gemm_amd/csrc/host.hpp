@@ -7,7 +7,6 @@
 #include <cstdint>
 
 #include "forge.h"
-#include "pingpong_kernels.hpp"
 #include "wgrad_kernels.hpp"
 
 namespace forge {
@@ -26,6 +25,9 @@ struct TileShape {
 TileShape shape_of(forge_tile t);
 int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s);
 double persistent_makespan(int64_t tiles, int grid);
+// The tile a call runs: `t`, or the library's choice for t = DEFAULT. Where
+// the persistent schedule is not allowed (grouped calls, the input gradient),
+// FORGE_TILE_PERSISTENT falls back to 256x256 tiles.
 forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts,
                         bool allow_persistent = true);
 forge_status launch_status();
@@ -38,16 +40,6 @@ bool grid_fits(int64_t d_in, int64_t d_out, forge_tile tile, int64_t experts);
 using Cfg256x256 = TileCfg<256, 256, 2, 2, 32, 1>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 1>;
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 32, 2>;
-// One wave group of the two-group kernel: 256x128 tiles, 4x1 waves of 64x128,
-// and the 128x128 halves a worker's odd last tile is split into.
-using CfgPP = TileCfg<256, 128, 4, 1, 32, 2>;
-using CfgPPHalf = TileCfg<128, 128, 4, 1, 32, 2>;
-// Row instructions of optimizer state in flight per wave in its epilogue.
-constexpr int kPPDepth = 6;
-// Ticks of the other group per epilogue row step, and whether a worker's odd
-// last tile is split between the groups.
-constexpr int kPPPace = 2;
-constexpr bool kPPSplit = false;
 
 template <class C>
 void set_grid(WgradArgs& a, int64_t experts) {
@@ -82,22 +74,6 @@ forge_status launch_persistent(WgradArgs a, hipStream_t s) {
   return launch_status();
 }
 
-// The two-group kernel (bf16 optimizer state keeps the persistent kernel's
-// wide epilogue).
-template <int EPI>
-forge_status launch_pingpong(WgradArgs a, hipStream_t s) {
-  if constexpr ((EPI & EPI_BF16_STATE) != 0) {
-    return launch_persistent<EPI>(a, s);
-  } else {
-    set_grid<CfgPP>(a, 1);
-    const int grid = persistent_grid();
-    if (grid <= 0) return launch_dense_t<Cfg256x128, EPI>(a, s);
-    hipLaunchKernelGGL((wgrad_pingpong_kernel<CfgPP, CfgPPHalf, EPI, kPPDepth, kPPPace, kPPSplit>), dim3(grid),
-                       dim3(2 * CfgPP::THREADS), 0, s, a);
-    return launch_status();
-  }
-}
-
 template <int EPI>
 forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
   switch (tile) {
@@ -105,7 +81,6 @@ forge_status launch_dense(const WgradArgs& a, forge_tile tile, hipStream_t s) {
     case FORGE_TILE_256x128: return launch_dense_t<Cfg256x128, EPI>(a, s);
     case FORGE_TILE_256x256: return launch_dense_t<Cfg256x256, EPI>(a, s);
     case FORGE_TILE_PERSISTENT: return launch_persistent<EPI>(a, s);
-    case FORGE_TILE_PINGPONG: return launch_pingpong<EPI>(a, s);
     default: return FORGE_ERR_TILE;
   }
 }
