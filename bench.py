@@ -32,7 +32,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA, twice the bf16 rate
-NOMINAL_CLOCK_GHZ = 2.4        # the clock the published peaks are quoted at
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused dW-GEMM+AdamW TFLOP/s & ms/step, MFMA util %, HBM bytes vs unfused"
 
@@ -112,13 +111,14 @@ def read_counters(workload: str, sha: str, n_param: int):
                         r"\s*([0-9.]+)\s*\|(?:\s*[0-9.eE+]+\s*\|\s*[0-9.]+\s*\|\s*([0-9.]+)\s*\|)?",
                         text, re.M)
         if m_sha and m_sha.group(1) == sha and m_b:
+            # busy cycles over the kernel's cycles at the clock it ran in the
+            # profiled run (the board holds it at its power limit); the bench's
+            # roofline fraction stays against the published peak
             out["mfma_busy_fraction"] = float(m_b.group(1))
             if m_b.group(2):
-                # The board holds this kernel at its power limit below the nominal
-                # clock; the busy fraction is against the peak at the clock it ran.
-                clock = float(m_b.group(2))
-                out["clock_ghz"] = clock
-                out["peak_tflops_at_clock"] = round(PEAK_BF16_TFLOPS * clock / NOMINAL_CLOCK_GHZ, 1)
+                out["profiled_clock_ghz"] = float(m_b.group(2))
+    if out:
+        out["from"] = f"profiles/pmc_{workload}.txt, pmc_mfma_{workload}.txt (committed)"
     return out or None
 
 
@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--workload", default="mlp_down", choices=sorted(WORKLOADS))
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--pool", type=int, default=2, help="distinct input batches cycled")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed fused steps for at least this long before the warm-up steps "
+                         "(the clock ramps for ~0.2 s after an idle period)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -242,6 +245,16 @@ def main():
         per = [a.elapsed_time(b) for a, b in ev]
         return total / steps, float(np.mean(per)), per
 
+    # After an idle period (input generation) the clock ramps for about 0.2 s
+    # under this load; untimed steps until it has settled, so the timed steps
+    # see the clock a continuously running training loop sees. Reported.
+    n_settle, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        for _ in range(8):
+            fused(n_settle + 1, batches[n_settle % len(batches)])
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t0
     ms_step, ms_kernel, per = timed(fused, args.steps, args.warmup)
     log(f"[bench] fused: {ms_step:.4f} ms/step, kernel avg {ms_kernel:.4f} ms "
         f"(min {min(per):.4f} max {max(per):.4f})")
@@ -314,10 +327,14 @@ def main():
             variants[name] = {"ms_per_step": round(v_step, 5),
                               "tflops": round(flops / v_step / 1e9, 2),
                               "alg_hbm_bytes": nbytes,
-                              "frac_bf16_peak": round(flops / v_step / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                              }
+            # each variant against the peak of the arithmetic it runs
             if "fp8" in name:
                 variants[name]["frac_fp8_peak"] = round(flops / v_step / 1e9 / PEAK_FP8_TFLOPS,
                                                         4)
+            else:
+                variants[name]["frac_bf16_peak"] = round(flops / v_step / 1e9 / PEAK_BF16_TFLOPS,
+                                                         4)
             log(f"[bench] {name}: {v_step:.4f} ms/step")
         del mb, vb, gb, fp8_batches
 
@@ -446,6 +463,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": n_settle, "seconds": round(settle_s, 3)},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

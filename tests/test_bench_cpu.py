@@ -55,8 +55,8 @@ def test_counters_read_when_the_sources_match(fake_profiles):
     assert bench.read_traffic("w", "abc123") == 3.0e9
     c = bench.read_counters("w", "abc123", 100_000_000)
     assert c == {"fused_write_bytes_per_param": 12.0, "unfused_pair_hbm_bytes": 3.7e9,
-                 "mfma_busy_fraction": 0.601, "clock_ghz": 1.8,
-                 "peak_tflops_at_clock": round(bench.PEAK_BF16_TFLOPS * 1.8 / 2.4, 1)}
+                 "mfma_busy_fraction": 0.601, "profiled_clock_ghz": 1.8,
+                 "from": "profiles/pmc_w.txt, pmc_mfma_w.txt (committed)"}
 
 
 def test_counters_dropped_when_the_sources_changed(fake_profiles):
