@@ -53,8 +53,9 @@
  * Determinism: every output element accumulates its tokens in ascending
  * order, 16 at a time, in one accumulator, with no split of the reduction
  * and no atomics. The result is therefore bitwise identical for every tile
- * choice, between fused and unfused paths, and from run to run (FORGE
- * assessment, P1: per-tile exactness is bitwise and partition independent).
+ * choice, between fused and unfused paths, and from run to run. (FORGE
+ * assessment, "Math verified, not asserted", P1: because each tile reduces
+ * its own whole sum, how the output is cut into tiles cannot change a bit.)
  */
 #ifndef FORGE_H
 #define FORGE_H
@@ -233,11 +234,12 @@ FORGE_API forge_status forge_grouped_wgrad_sgdm(const void* X_perm, const void* 
 
 /*
  * Precision variants. FORGE assessment, "What's already in tree and easy to
- * miss": the existing lowering accumulates a bf16 matmul in float32 and then
- * truncates to bf16, and that truncation is exactly the rounding the fused
- * path deletes; "Math verified, not asserted", P6: the float32-accumulator
- * benefit is worth ~900x with float32 optimizer state and ~1x with bf16
- * state. These calls make every combination measurable on the GPU.
+ * miss": today's lowering rounds the float32 accumulator of the bf16 matmul
+ * to a bf16 gradient, and the fused path removes that rounding step;
+ * "Math verified, not asserted", P6: keeping the float32 accumulator pays
+ * off by a large factor (~900x) when the optimizer state is float32 and
+ * hardly at all (~1x) when the state itself is bf16. These calls make every
+ * combination measurable on the GPU.
  *
  * forge_wgrad_bf16: the unfused gradient, rounded to bf16 (nearest even)
  *   from the same float32 accumulator forge_wgrad stores; grad_bf16 is
@@ -363,9 +365,15 @@ FORGE_API forge_status forge_wgrad_sgdm_bf16w(const void* X, const void* dY, flo
  *   x_scale, dy_scale: per-tensor dequantization scales (value = code value x
  *   scale); both finite and > 0, and their product, rounded to float32, a
  *   normal float32 (else FORGE_ERR_HPARAM).
- * The gradient is g = float32(x_scale dy_scale) times the float32 sum of the
- * code-value products over all tokens (each product is exact), i.e. the
- * scale is applied once to the accumulator. forge_wgrad_fp8 stores g
+ * The gradient is g = float32(x_scale dy_scale) times the float32
+ * accumulation of the code-value products over all tokens, i.e. the scale is
+ * applied once to the accumulator. The fp8 matrix instruction does not form
+ * the products exactly: within each run of 8 consecutive tokens it truncates
+ * every product toward zero to a multiple of 2^(E-13), E being the largest
+ * exponent sum e_x + e_dy over the run's nonzero products, and adds the run's
+ * truncated products into the float32 accumulator. A product of codes whose
+ * exponents sit far below the run's largest can therefore lose all its bits.
+ * forge_wgrad_fp8 stores g
  * (float32, [d_out, d_in]); forge_wgrad_adamw_fp8 consumes it in the AdamW
  * epilogue exactly as forge_wgrad_adamw does. Tokens enter in ascending
  * chunks of 64, so every tiling gives the same bits. Contract otherwise as
