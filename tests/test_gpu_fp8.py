@@ -19,7 +19,8 @@ import synth
 from oracle import lowp
 from synth import DenseCase
 from tests._fp8_runs import HAND_PAIRS, HAND_RUNS, hand_pair_inputs, hand_run_inputs
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, log,
+from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev,
+                        fp8_model_reference, host, log,
                         torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -227,6 +228,7 @@ def test_fused_adamw_fp8(wg, tile):
     W0, m0, v0 = synth.dense_state(case)
     W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
     par = AdamWParity(W0, m0, v0, hp, ambiguous_budget=None)
+    par_model = AdamWParity(W0, m0, v0, hp)
     for t in range(1, case.steps + 1):
         X8, sx, dY8, sdy = _inputs(case, t, "e4m3", "e5m2")
         log(f"[{case.name}] fp8 adamw step {t} tile {tile}")
@@ -234,11 +236,15 @@ def test_fused_adamw_fp8(wg, tile):
         wg.forge_wgrad_adamw_fp8(u8_dev(X8), "e4m3", sx, u8_dev(dY8), "e5m2", sdy, W, m, v,
                                  step=t, tile=tile, **hp)
         _sync()
+        state = host(W), host(m), host(v)
         rep = par.step(t, lowp.wgrad_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy),
-                       lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy), W_prev, host(W),
-                       host(m), host(v))
-        log(f"  {rep}")
+                       lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy), W_prev, *state)
+        log(f"  exact gradient, fp8 floor: {rep}")
         assert rep.passed, f"step {t}: {rep}"
+        g_mod, tau_mod = fp8_model_reference(X8, "e4m3", sx, dY8, "e5m2", sdy)
+        rep = par_model.step(t, g_mod, tau_mod, W_prev, *state)
+        log(f"  model gradient, fp32 floor: {rep}")
+        assert rep.passed, f"step {t} (model): {rep}"
 
 
 def test_fused_adamw_fp8_equals_unfused(wg):

@@ -13,7 +13,8 @@ import pytest
 import oracle
 import synth
 from oracle import judge
-from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
+from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev,
+                        fp8_model_reference, host,
                         host_f32,
                         log, run_dense_adamw, run_dense_sgdm, sample_rows, torch_mod)
 
@@ -131,6 +132,7 @@ def test_mlp_down_fp8_adamw(wg):
     W0, m0, v0 = synth.dense_state(case)
     W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
     par = AdamWParity(W0, m0, v0, hp, rows=rows, ambiguous_budget=None)
+    par_model = AdamWParity(W0, m0, v0, hp, rows=rows)
     for t in range(1, 4):
         X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, t)
         log(f"[{case.name}] fp8 adamw step {t}")
@@ -141,9 +143,14 @@ def test_mlp_down_fp8_adamw(wg):
         torch.cuda.synchronize()
         g_ref = lowp.wgrad_fp8(X8, "e4m3", sx, np.ascontiguousarray(dY8[:, rows]), "e5m2", sdy)
         tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows)
-        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
-        log(f"  {rep}")
+        state = host(W, rows), host(m, rows), host(v, rows)
+        rep = par.step(t, g_ref, tau, W_prev, *state)
+        log(f"  exact gradient, fp8 floor: {rep}")
         assert rep.passed, f"step {t}: {rep}"
+        g_mod, tau_mod = fp8_model_reference(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows)
+        rep = par_model.step(t, g_mod, tau_mod, W_prev, *state)
+        log(f"  model gradient, fp32 floor: {rep}")
+        assert rep.passed, f"step {t} (model): {rep}"
 
 
 def test_lm_head_fp8_adamw(wg):
@@ -160,6 +167,7 @@ def test_lm_head_fp8_adamw(wg):
     W0, m0, v0 = synth.dense_state(case)
     W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
     par = AdamWParity(W0, m0, v0, hp, rows=rows, ambiguous_budget=None)
+    par_model = AdamWParity(W0, m0, v0, hp, rows=rows)
     for t in range(1, 2):
         X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, t)
         log(f"[{case.name}] fp8 adamw step {t}")
@@ -170,9 +178,14 @@ def test_lm_head_fp8_adamw(wg):
         torch.cuda.synchronize()
         g_ref = lowp.wgrad_fp8(X8, "e4m3", sx, np.ascontiguousarray(dY8[:, rows]), "e5m2", sdy)
         tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows)
-        rep = par.step(t, g_ref, tau, W_prev, host(W, rows), host(m, rows), host(v, rows))
-        log(f"  {rep}")
+        state = host(W, rows), host(m, rows), host(v, rows)
+        rep = par.step(t, g_ref, tau, W_prev, *state)
+        log(f"  exact gradient, fp8 floor: {rep}")
         assert rep.passed, f"step {t}: {rep}"
+        g_mod, tau_mod = fp8_model_reference(X8, "e4m3", sx, dY8, "e5m2", sdy, rows=rows)
+        rep = par_model.step(t, g_mod, tau_mod, W_prev, *state)
+        log(f"  model gradient, fp32 floor: {rep}")
+        assert rep.passed, f"step {t} (model): {rep}"
 
 
 def test_qkv_adamw_and_sgdm(wg):
