@@ -146,3 +146,53 @@ def test_grouped_adamw_replay(wg):
 
     g = _capture(steps)
     _replay_and_check(g, [W, m, v], initial, expected, lambda: None)
+
+
+# fp8 inputs need d_in and d_out multiples of 16
+CASE16 = DenseCase("graph_300x528x400", T=300, d_in=528, d_out=400, seed_base=66000)
+
+
+@pytest.mark.parametrize("kind", ["sgdm", "bf16_state", "fp8_adamw"])
+def test_other_fused_steps_replay(wg, kind):
+    """The other fused epilogues in a graph: SGD-momentum, AdamW with bf16
+    moments, and AdamW from fp8 inputs (three steps each)."""
+    torch = torch_mod()
+    case = CASE16
+    hp = adamw_hp(case)
+    W0, m0, v0 = synth.dense_state(case)
+    if kind == "fp8_adamw":
+        batches = []
+        for t in STEPS:
+            X8, sx, dY8, sdy = synth.dense_inputs_fp8(case, t)
+            batches.append((torch.from_numpy(X8).to("cuda"), sx, torch.from_numpy(dY8).to("cuda"),
+                            sdy))
+    else:
+        batches = [tuple(bf16_dev(a) for a in synth.dense_inputs(case, t)) for t in STEPS]
+    sdt = torch.bfloat16 if kind == "bf16_state" else torch.float32
+    log(f"[{case.name}] graph of {len(STEPS)} steps: {kind}")
+
+    def state():
+        W = f32_dev(W0)
+        m = torch.zeros(W.shape, device="cuda", dtype=sdt)
+        v = torch.zeros(W.shape, device="cuda", dtype=sdt)
+        return [W, m, v]
+
+    def run(W, m, v):
+        for t, b in zip(STEPS, batches):
+            if kind == "sgdm":
+                wg.forge_wgrad_sgdm(b[0], b[1], W, m, lr=hp["lr"], momentum=0.9,
+                                    weight_decay=hp["weight_decay"])
+            elif kind == "bf16_state":
+                wg.forge_wgrad_adamw_bf16state(b[0], b[1], W, m, v, step=t, **hp)
+            else:
+                wg.forge_wgrad_adamw_fp8(b[0], "e4m3", b[1], b[2], "e5m2", b[3], W, m, v,
+                                         step=t, **hp)
+
+    eager = state()
+    run(*eager)
+    torch.cuda.synchronize()
+    expected = [host_f32(t) for t in eager]
+    live = state()
+    initial = state()
+    g = _capture(lambda: run(*live))
+    _replay_and_check(g, live, initial, expected, lambda: run(*state()))
