@@ -83,6 +83,7 @@ def call_adamw(lib, X=X_ADDR, dY=Y_ADDR, W=A, m=B, v=C, T=64, d_in=64, d_out=32,
 @pytest.mark.parametrize("kw,status", [
     (dict(W=NULL), 1), (dict(m=NULL), 1), (dict(v=NULL), 1), (dict(X=NULL), 1), (dict(dY=NULL), 1),
     (dict(T=-1), 2), (dict(d_in=-8), 2), (dict(d_out=-8), 2), (dict(T=1 << 31), 2),
+    (dict(d_in=(1 << 22) + 8), 2), (dict(d_out=(1 << 22) + 8), 2),
     (dict(d_in=12), 3), (dict(d_out=20), 3), (dict(W=A + 4), 3), (dict(X=X_ADDR + 2), 3),
     (dict(dY=Y_ADDR + 8), 3),
     (dict(m=A), 4), (dict(v=A + 64), 4), (dict(W=X_ADDR), 4), (dict(m=Y_ADDR - 16), 4),

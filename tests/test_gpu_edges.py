@@ -7,6 +7,10 @@
 - The smallest shapes the ABI accepts (d_in and d_out multiples of 8, one to
   a few tokens), on every tile id, against the oracle: every tile is a tail in
   both directions and the token loop has a single partial stage.
+- The largest d_in and the largest d_out the ABI accepts (2^22), each with the
+  other dimension at its smallest, a ragged token count and every element
+  judged: the largest stage rows and state rows the 32-bit buffer windows
+  hold, and 16384 tiles along one axis.
 """
 import numpy as np
 import pytest
@@ -14,8 +18,9 @@ import pytest
 import oracle
 import synth
 from synth import DenseCase
+from oracle import judge
 from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
-                        log, torch_mod)
+                        host_f32, log, run_dense_adamw, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +95,27 @@ def test_smallest_shapes(wg, T, d_in, d_out, tile):
     _sync()
     err = np.abs(host(g).astype(np.float64) - oracle.wgrad_f64(Xb, dYb))
     assert np.all(err <= oracle.acc_floor(Xb, dYb))
+
+
+MAX_DIM = 1 << 22                                     # the ABI's largest d_in and d_out
+
+
+@pytest.mark.parametrize("d_in,d_out", [(MAX_DIM, 8), (8, MAX_DIM)], ids=["max_d_in", "max_d_out"])
+@pytest.mark.parametrize("tile", [0, 3])
+def test_largest_dims(wg, d_in, d_out, tile):
+    torch = torch_mod()
+    case = DenseCase(f"maxdim_33x{d_in}x{d_out}", T=33, d_in=d_in, d_out=d_out,
+                     seed_base=68000 + (d_in > d_out), steps=2)
+    W, _, _ = run_dense_adamw(wg, case, 2, tile=tile)
+    # the input gradient from the updated weight (K = d_out up to 2^22)
+    Xb, dYb = synth.dense_inputs(case, 3)
+    W_host = host(W)
+    dX = torch.full((case.T, d_in), float("nan"), device="cuda", dtype=torch.bfloat16)
+    log(f"[{case.name}] dX, tile {tile}")
+    wg.forge_dgrad(bf16_dev(dYb), W, dX, tile=0 if tile == 0 else 3)
+    _sync()
+    rep = judge.judge_dgrad(host_f32(dX), dYb, W_host, True)
+    assert rep.passed, str(rep)
 
 
 def test_tensor_on_another_device_is_refused(wg, monkeypatch):
