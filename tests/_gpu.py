@@ -136,11 +136,11 @@ def bits_equal(a, b) -> bool:
     return judge.bitwise_equal(a, b)
 
 
-def run_dense_adamw(wg, case, steps, tile=0, rows=None):
+def run_dense_adamw(wg, case, steps, tile=0, rows=None, ambiguous_budget=AMBIGUOUS_BUDGET):
     """AdamW steps of `case` on the GPU, judged against the oracle each step."""
     W0, m0, v0 = synth.dense_state(case)
     W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
-    par = AdamWParity(W0, m0, v0, adamw_hp(case), rows=rows)
+    par = AdamWParity(W0, m0, v0, adamw_hp(case), rows=rows, ambiguous_budget=ambiguous_budget)
     for t in range(1, steps + 1):
         log(f"[{case.name}] adamw step {t} tile {tile}")
         Xb, dYb = synth.dense_inputs(case, t)

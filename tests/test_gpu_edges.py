@@ -10,7 +10,7 @@
 - The largest d_in and the largest d_out the ABI accepts (2^22), each with the
   other dimension at its smallest, a ragged token count and every element
   judged: the largest stage rows and state rows the 32-bit buffer windows
-  hold, and 16384 tiles along one axis.
+  hold, and 16384 tiles along one axis; and 2^22 + 17 tokens on a small layer.
 """
 import numpy as np
 import pytest
@@ -116,6 +116,19 @@ def test_largest_dims(wg, d_in, d_out, tile):
     _sync()
     rep = judge.judge_dgrad(host_f32(dX), dYb, W_host, True)
     assert rep.passed, str(rep)
+
+
+@pytest.mark.parametrize("tile", [0, 3])
+def test_many_tokens(wg, tile):
+    """2^22 + 17 tokens (131073 stages of one tile, the last one partial) on a
+    small layer: the stage counters and running pointers over a long token
+    loop, every element judged. No budget on widened weight-delta bars: the
+    float32 floor grows like sqrt(T) against a random gradient (here ~5e-4 of
+    it), so at step 2 a correct float32 order can move an ordinary element's
+    update by ~1e-3 lr, and a fifth of these 128 weights are ambiguous."""
+    case = DenseCase("manytok_4194321x16x8", T=(1 << 22) + 17, d_in=16, d_out=8,
+                     seed_base=68100, steps=2)
+    run_dense_adamw(wg, case, 2, tile=tile, ambiguous_budget=None)
 
 
 def test_tensor_on_another_device_is_refused(wg, monkeypatch):
