@@ -86,10 +86,6 @@ int64_t count_tiles(int64_t d_in, int64_t d_out, TileShape s) {
   return ((d_in + s.bm - 1) / s.bm) * ((d_out + s.bn - 1) / s.bn);
 }
 
-// Default tile: the one with the best estimated throughput for the shape. A
-// tile's share of the matrix-core rate (measured on gfx950 for the
-// Llama-3-8B MLP-down contraction, relative to 256x256) is scaled by how well
-// its tiles fill whole waves of workgroups over the 256 compute units.
 // Makespan, in full-tile times, of the persistent schedule for `tiles` 256x256
 // tiles on `grid` workgroups (odd XCDs half a tile behind). A half tile costs
 // 0.6 of a full one (it runs at ~85% of the full tile's rate).
@@ -110,6 +106,11 @@ double persistent_makespan(int64_t tiles, int grid) {
   return worst;
 }
 
+// Default tile: the one with the best estimated throughput for the shape. A
+// tile's share of the matrix-core rate (measured on gfx950 for the
+// Llama-3-8B MLP-down contraction, relative to 256x256) is scaled by how well
+// its tiles fill whole waves of workgroups over the 256 compute units; the
+// persistent schedule is scored by its makespan.
 forge_tile resolve_tile(forge_tile t, int64_t d_in, int64_t d_out, int64_t experts,
                         bool allow_persistent) {
   if ((experts > 1 || !allow_persistent) && t == FORGE_TILE_PERSISTENT) return FORGE_TILE_256x256;
