@@ -245,6 +245,40 @@ def test_grouped_small_with_empty_experts(wg, tile):
         assert not bits_equal(Wg[1], W_prev[1])   # the empty expert still moved
 
 
+def test_grouped_most_experts(wg):
+    """FORGE_MAX_EXPERTS (256) experts in one call, a fifth of them empty and
+    the rest with 1 to 12 rows, on a small layer: the whole expert table goes
+    to the kernel by value; every expert judged against the oracle over two
+    steps from a warm state, and two tilings bitwise equal."""
+    E, d_in, d_out = 256, 24, 16
+    rng = np.random.default_rng(88)
+    counts = rng.integers(1, 13, size=E)
+    counts[rng.random(E) < 0.2] = 0
+    offsets = [0] + [int(x) for x in np.cumsum(counts)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(89, (E, d_out, d_in), 0.02)
+    m0 = synth.normal_f32(90, W0.shape, 0.01)
+    v0 = np.abs(synth.normal_f32(91, W0.shape, 1e-3))
+    states = {tl: [f32_dev(W0), f32_dev(m0), f32_dev(v0)] for tl in (1, 3)}
+    pars = [AdamWParity(W0[e], m0[e], v0[e], hp) for e in range(E)]
+    for t in (1, 2):
+        log(f"[grouped E={E}] step {t}, {offsets[-1]} rows")
+        Xb = synth.normal_bf16(92 + t, (offsets[-1], d_in))
+        dYb = synth.normal_bf16(94 + t, (offsets[-1], d_out))
+        W_prev = host(states[3][0])
+        for tl, (W, m, v) in states.items():
+            run_grouped(wg, Xb, dYb, offsets, W, m, v, t, hp, tile=tl)
+        _sync()
+        Wg, mg, vg = (host(a) for a in states[3])
+        assert all(bits_equal(host(a), b) for a, b in zip(states[1], (Wg, mg, vg)))
+        grads = oracle.grouped_wgrad(Xb, dYb, offsets)
+        for e in range(E):
+            a, b = offsets[e], offsets[e + 1]
+            tau = oracle.acc_floor(Xb[a:b], dYb[a:b]) if b > a else np.zeros((d_out, d_in))
+            rep = pars[e].step(t, grads[e], tau, W_prev[e], Wg[e], mg[e], vg[e])
+            assert rep.passed, f"expert {e} step {t}: {rep}"
+
+
 @pytest.mark.parametrize("tile", [0, 4])
 def test_grouped_single_expert(wg, tile):
     """A grouped call with one expert on a shape of 256 full 256x256 tiles
