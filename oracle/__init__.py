@@ -14,13 +14,18 @@ ships AdamW and SGD only). Fusion changes where the gradient lives, not its
 value (section "Math verified, not asserted", P1), so the unfused definition
 is the reference for the fused kernels.
 
-fp8 inputs (the paper's fp8 row in P6) are in ``lowp.py``. The precision variants of P6 (a bf16-rounded gradient, bf16 moments) and the
+fp8 inputs (the paper's fp8 row in P6) are in ``lowp.py``, with the model of
+the fp8 matrix instruction's dot product (its C helper is ``fp8_dot.c``). The
+precision variants of P6 (a bf16-rounded gradient, bf16 moments) and the
 float64 reference they are measured against are in ``ref.py`` too; the P6
 study itself in ``precision_study.py``.
 
 Parity pins (tests that check this package against closed forms, exact
-rational arithmetic and invariants) live in tests/test_oracle_pins.py and
-tests/test_precision_oracle.py.
+rational arithmetic, hand-worked examples and invariants) live in
+tests/test_oracle_pins.py, tests/test_precision_oracle.py,
+tests/test_dgrad_oracle.py and tests/test_fp8_oracle.py; the fp8 model's two
+constants are pinned bit for bit against the instruction by GPU regression
+tests on designed inputs (tests/test_gpu_fp8.py).
 Parity unpinned: the exact summation order inside the GPU contraction (only
 the accumulation floor in ``floor.py`` bounds it), and the magnitudes the page
 quotes without their setups (2.24x at 50% routing; ~900x / ~1x, which the
