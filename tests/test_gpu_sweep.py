@@ -5,10 +5,13 @@ their tails by hand; this sweep walks residues of every tile and stage size
 (256, 128, 64, 32, 16, 8) that they do not.
 
 Per shape: one fused AdamW step (W, m, v judged element by element against
-the oracle's step on its exact gradient), the input gradient from the float32
-weight (judged) and from its bf16 copy (bitwise the same); and, on the same
-shapes rounded up to multiples of 16, the fp8-input gradient (judged against
-the exact fp8 sum).
+the oracle's step on its exact gradient), one fused SGD-momentum step with
+weight decay (judged the same way), the input gradient from the float32
+weight (judged) and from its bf16 copy (bitwise the same); on the same shapes
+rounded up to multiples of 16, the fp8-input gradient (judged against the
+exact fp8 sum, and against the model of the fp8 instruction with the float32
+floor alone). A second sweep draws routed-expert calls: 1 to 12 experts with
+random row counts (some empty) on random layers, every expert judged.
 """
 import numpy as np
 import pytest
@@ -17,8 +20,8 @@ import oracle
 import synth
 from oracle import judge, lowp
 from synth import DenseCase
-from tests._gpu import (AdamWParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host, host_f32,
-                        log, torch_mod)
+from tests._gpu import (AdamWParity, SgdmParity, adamw_hp, bf16_dev, bits_equal, f32_dev, host,
+                        host_f32, log, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +74,18 @@ def test_sweep_fused_adamw_and_dgrad(wg, case, tile):
     wg.forge_wgrad_adamw(X, dY, W, m, v, step=1, tile=tile, **hp)
     torch.cuda.synchronize()
     par = AdamWParity(W0, m0, v0, hp)
-    rep = par.step(1, oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb), W0, host(W), host(m),
-                   host(v))
+    g_ref, tau = oracle.wgrad(Xb, dYb), oracle.acc_floor(Xb, dYb)
+    rep = par.step(1, g_ref, tau, W0, host(W), host(m), host(v))
+    assert rep.passed, str(rep)
+
+    log(f"[{case.name}] fused SGD-momentum step, tile {tile}")
+    hs = dict(lr=case.lr, momentum=case.momentum, weight_decay=0.01)
+    b0 = synth.normal_f32(case.seed_base + 7, W0.shape, 1e-3)      # a momentum history
+    W, b = f32_dev(W0), f32_dev(b0)
+    wg.forge_wgrad_sgdm(X, dY, W, b, tile=tile, **hs)
+    torch.cuda.synchronize()
+    spar = SgdmParity(W0, b0, hs)
+    rep = spar.step(g_ref, tau, W0, host(W), host(b))
     assert rep.passed, str(rep)
 
 
@@ -98,3 +111,50 @@ def test_sweep_fp8_gradient(wg, case, tile):
     err = np.abs(host(g).astype(np.float64) - ref)
     tau = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy)
     assert np.all(err <= tau), f"max err / floor {np.max(err / tau):.3f}"
+    model = lowp.mfma_fp8_dot(X8, "e4m3", dY8, "e5m2") * float(np.float32(sx * sdy))
+    inner = lowp.acc_floor_fp8(X8, "e4m3", sx, dY8, "e5m2", sdy, dot_loss=False)
+    err_m = np.abs(host(g).astype(np.float64) - model)
+    assert np.all(err_m <= inner), f"model: max err / fp32 floor {np.max(err_m / inner):.3f}"
+
+
+def _grouped_cases(n=16, seed=4048):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        E = int(rng.integers(1, 13))
+        counts = rng.integers(0, 200, size=E)
+        counts[rng.random(E) < 0.25] = 0
+        d_in = 8 * int(rng.integers(1, 49))
+        d_out = 8 * int(rng.integers(1, 49))
+        tile = int(rng.choice([0, 1, 2, 3]))
+        out.append((k, [0] + [int(x) for x in np.cumsum(counts)], d_in, d_out, tile))
+    return out
+
+
+GROUPED = _grouped_cases()
+
+
+@pytest.mark.parametrize("k,offsets,d_in,d_out,tile", GROUPED,
+                         ids=[f"g{k}_E{len(o) - 1}_R{o[-1]}_{di}x{do}_t{t}"
+                              for k, o, di, do, t in GROUPED])
+def test_sweep_grouped_adamw(wg, k, offsets, d_in, d_out, tile):
+    E = len(offsets) - 1
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    W0 = synth.normal_f32(90000 + 10 * k, (E, d_out, d_in), 0.02)
+    m0 = synth.normal_f32(90001 + 10 * k, W0.shape, 0.01)
+    v0 = np.abs(synth.normal_f32(90002 + 10 * k, W0.shape, 1e-3))
+    Xb = synth.normal_bf16(90003 + 10 * k, (offsets[-1], d_in))
+    dYb = synth.normal_bf16(90004 + 10 * k, (offsets[-1], d_out))
+    log(f"[grouped sweep {k}] E {E}, rows {offsets[-1]}, {d_in}x{d_out}, tile {tile}")
+    W, m, v = f32_dev(W0), f32_dev(m0), f32_dev(v0)
+    wg.forge_grouped_wgrad_adamw(bf16_dev(Xb), bf16_dev(dYb), offsets, W, m, v, step=3,
+                                 tile=tile, **hp)
+    torch_mod().cuda.synchronize()
+    Wg, mg, vg = host(W), host(m), host(v)
+    grads = oracle.grouped_wgrad(Xb, dYb, offsets)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        tau = oracle.acc_floor(Xb[a:b], dYb[a:b]) if b > a else np.zeros((d_out, d_in))
+        par = AdamWParity(W0[e], m0[e], v0[e], hp)
+        rep = par.step(3, grads[e], tau, W0[e], Wg[e], mg[e], vg[e])
+        assert rep.passed, f"expert {e}: {rep}"
