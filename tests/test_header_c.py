@@ -58,3 +58,39 @@ def test_header_compiles_and_links_as_c(tmp_path, std):
     status, *rest = out.stdout.split()
     assert int(status) == 6                       # FORGE_ERR_CLIP_NOT_FUSABLE
     assert int(rest[-1]) == len(names)
+
+
+def test_binding_constants_match_the_header(tmp_path):
+    """The Python binding's tile ids, element types, status codes and struct
+    layouts are the header's: a C program prints the header's values and
+    sizes, and they must equal the binding's."""
+    import ctypes
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = (["FORGE_TILE_DEFAULT", "FORGE_TILE_256x128", "FORGE_TILE_128x128",
+              "FORGE_TILE_256x256", "FORGE_TILE_PERSISTENT", "FORGE_F32", "FORGE_BF16",
+              "FORGE_FP8_E4M3", "FORGE_FP8_E5M2"] + sorted(_lib.STATUS.values()))
+    src = tmp_path / "consts.c"
+    src.write_text(
+        "#include \"forge.h\"\n#include <stdio.h>\n#include <stddef.h>\n"
+        "int main(void) {\n"
+        + "".join(f"  printf(\"{n} %d\\n\", (int){n});\n" for n in names)
+        + "  printf(\"adamw_size %d\\n\", (int)sizeof(forge_adamw_params));\n"
+          "  printf(\"adamw_step %d\\n\", (int)offsetof(forge_adamw_params, step));\n"
+          "  printf(\"adamw_clip %d\\n\", (int)offsetof(forge_adamw_params, max_grad_norm));\n"
+          "  printf(\"sgdm_size %d\\n\", (int)sizeof(forge_sgdm_params));\n"
+          "  return 0;\n}\n")
+    exe = tmp_path / "consts"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = dict((k, int(v)) for k, v in (ln.split() for ln in out.splitlines()))
+    for n in names[:9]:
+        assert got[n] == getattr(_lib, n), n
+    for code, n in _lib.STATUS.items():
+        assert got[n] == code, n
+    assert got["adamw_size"] == ctypes.sizeof(_lib.AdamWParams)
+    assert got["adamw_step"] == _lib.AdamWParams.step.offset
+    assert got["adamw_clip"] == _lib.AdamWParams.max_grad_norm.offset
+    assert got["sgdm_size"] == ctypes.sizeof(_lib.SgdmParams)
