@@ -140,6 +140,10 @@ def main():
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="untimed fused steps for at least this long before the warm-up steps "
                          "(the clock ramps for ~0.2 s after an idle period)")
+    ap.add_argument("--leg-settle-s", type=float, default=0.1,
+                    help="untimed steps of each comparison leg (unfused pair, precision "
+                         "variants, backward) for at least this long before its warm-up steps "
+                         "(the clock moves when the load changes kind)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -225,7 +229,13 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def timed(fn, steps, warmup, per_launch_events=True):
+    def timed(fn, steps, warmup, settle_s=0.0):
+        n, t_s = 0, time.perf_counter()
+        while time.perf_counter() - t_s < settle_s:
+            for _ in range(4):
+                fn(n + 1, batches[n % len(batches)])
+                n += 1
+            torch.cuda.synchronize()
         for s in range(warmup):
             fn(s + 1, batches[s % len(batches)])
         torch.cuda.synchronize()
@@ -278,7 +288,7 @@ def main():
             else:
                 wg.forge_sgdm(grad, W, m, **hp)
 
-        u_step, u_kernel, _ = timed(unfused_step, args.steps, args.warmup)
+        u_step, u_kernel, _ = timed(unfused_step, args.steps, args.warmup, args.leg_settle_s)
         unfused = {"ms_per_step": round(u_step, 5), "tflops": round(flops / u_step / 1e9, 2),
                    "alg_hbm_bytes": alg_bytes + 8 * n_param,
                    "fused_speedup": round(u_step / ms_step, 4)}
@@ -323,7 +333,7 @@ def main():
                                   x_bytes + 28 * n_param),
                                  ("fused_adamw_fp8_inputs", fused_fp8,
                                   x_bytes // 2 + 24 * n_param)):
-            v_step, v_kernel, _ = timed(fn, args.steps, args.warmup)
+            v_step, v_kernel, _ = timed(fn, args.steps, args.warmup, args.leg_settle_s)
             variants[name] = {"ms_per_step": round(v_step, 5),
                               "tflops": round(flops / v_step / 1e9, 2),
                               "alg_hbm_bytes": nbytes,
@@ -366,7 +376,7 @@ def main():
         backward = {}
         for name, fn, nbytes in (("dgrad", dgrad_only, dx_bytes + 4 * n_param),
                                  ("dgrad_bf16_copy", dgrad_copy, dx_bytes + 2 * n_param)):
-            d_step, d_kernel, _ = timed(fn, args.steps, args.warmup)
+            d_step, d_kernel, _ = timed(fn, args.steps, args.warmup, args.leg_settle_s)
             backward[name] = {"ms_per_step": round(d_step, 5), "kernel_ms": round(d_kernel, 5),
                               "tflops": round(flops / d_kernel / 1e9, 2),
                               "frac_bf16_peak": round(flops / d_kernel / 1e9 / PEAK_BF16_TFLOPS,
@@ -375,7 +385,7 @@ def main():
             log(f"[bench] {name}: {d_step:.4f} ms/step")
         for name, fn in (("linear_backward_adamw", linear_backward),
                          ("linear_backward_adamw_bf16_copy", linear_backward_copy)):
-            b_step, _, _ = timed(fn, args.steps, args.warmup)
+            b_step, _, _ = timed(fn, args.steps, args.warmup, args.leg_settle_s)
             backward[name] = {"ms_per_step": round(b_step, 5),
                               "tflops": round(2 * flops / b_step / 1e9, 2)}
             log(f"[bench] {name}: {b_step:.4f} ms/step")
@@ -463,7 +473,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle": {"steps": n_settle, "seconds": round(settle_s, 3)},
+        "settle": {"steps": n_settle, "seconds": round(settle_s, 3),
+                   "per_comparison_leg_s": args.leg_settle_s},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
